@@ -1,0 +1,229 @@
+"""Benchmark of one absorbed split-KV MLA decode step on one MI355X.
+
+Default workload: B=32, H=128, q_len=1, L=32768 per sequence, paged latent
+cache (block 32, blocks in a seeded random permutation), keys split into 8
+contiguous parts of 4096 (decode context parallelism emulated on one GPU),
+bf16 partial outputs and LSEs, LSE combine, V-up. One step = q-absorb +
+partial attention over all parts + LSE combine + V-up, inputs resident in
+HBM. Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode µs/step, TFLOP/s & KV GB/s (% roofline) at B=32 H=128 L=32K"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+KERNEL_SRC = os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", "partial_mfma.hip")
+PMC_FILE = os.path.join(ROOT, "profiles", "partial_mfma_kernel_pmc.json")
+
+
+def kernel_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch of the partial kernel from committed rocprofv3
+    counter runs, if they were taken on the current kernel source."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_sha") != kernel_hash() or d.get("workload") != workload:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s: float = 15.0):
+    """The float64 oracle on a bounded sample of (sequence, head) pairs of the
+    same workload, scaled to microseconds per full step."""
+    import oracle.mla_oracle as mo
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    sp = w.spec
+    qn, qr = w.f64("q_nope"), w.f64("q_rope")
+    wuk, wuv = w.f64("w_uk"), w.f64("w_uv")
+    cur = (lambda b: w.cur_rows64(b)) if sp.current else None
+    r = np.random.Generator(np.random.PCG64(11))
+    pairs = [(int(b), int(h)) for b, h in zip(r.integers(0, sp.B, 10_000),
+                                               r.integers(0, sp.H, 10_000))]
+    done, keys = 0, 0
+    rows_cache = {}
+    t0 = time.perf_counter()
+    for b, h in pairs:
+        if b not in rows_cache:
+            rows_cache.clear()
+            rows_cache[b] = w.seq_rows64(b)
+        mo.mla_decode_step(qn, qr, lambda bb: rows_cache[bb], wuk, wuv, sp.scale, sp.S,
+                           cur_rows=cur, seqs=[b], heads=[h])
+        done += 1
+        keys += int(w.lengths[b])
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    total_pairs = sp.B * sp.H
+    us_step = el / done * total_pairs * 1e6
+    return {"value": round(us_step, 1), "unit": "us/step", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {total_pairs} (sequence, head) pairs of the same workload "
+                      f"(float64, per-head K/V materialised), {el:.1f} s, scaled by "
+                      f"{total_pairs}/{done}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the DCP parts are processed on the one device", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from mla_split_kv_absorbed_amd import _lib as L
+    from mla_split_kv_absorbed_amd import workloads as W
+    from mla_split_kv_absorbed_amd.step import DecodeStep
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    L.lib()  # fail loudly if the HIP library is missing
+    sp = W.SPECS[args.workload]
+    print(f"[bench] generating workload {sp.name}", file=sys.stderr, flush=True)
+    w = W.make_workload(sp)
+    st = DecodeStep(w, device="cuda:0")
+    work = W.step_work(w)
+    stream = torch.cuda.current_stream()
+
+    # one shard alone: the first part's ranges, a single-part call
+    share = DecodeStep.__new__(DecodeStep)
+    one_args = L.partial_args(st.q_lat, st.q_rope, st.kv, st.range_start[:1].contiguous(),
+                              st.range_end[:1].contiguous(), st.parts_out[:1],
+                              st.parts_lse[:1], B=sp.B, S=sp.S, H=sp.H, scale=sp.scale,
+                              **({"block_table": st.block_table, "block_size": sp.block_size,
+                                  "num_blocks": w.kv.shape[0]} if sp.block_size else
+                                 {"kv_seq_stride": w.kv.shape[1]}))
+    one_ws = torch.empty(max(1, L.mla_decode_partial_workspace_size(one_args)),
+                         dtype=torch.uint8, device="cuda:0")
+    one_args.workspace, one_args.workspace_bytes = one_ws.data_ptr(), one_ws.numel()
+    del share
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        st.run(stream)
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for i in range(args.steps):
+        if st.absorb:
+            L.mla_q_absorb(st.q_nope, st.w_uk, st.q_lat, stream)
+        ev[i][0].record(stream)
+        L.mla_decode_partial(st.hist_args, stream)
+        ev[i][1].record(stream)
+        if sp.current:
+            L.mla_decode_partial(st.cur_args, stream)
+        if st.skip_combine:
+            x = st.parts_out[0]
+        else:
+            L.mla_lse_combine(st.parts_out, st.parts_lse, st.lat, st.lse,
+                              local_out=st.cur_out if sp.current else None,
+                              local_lse=st.cur_lse if sp.current else None, stream=stream)
+            x = st.lat
+        L.mla_vup(x, st.w_uv, st.out, stream)
+    e_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e_start.elapsed_time(e_end) / args.steps
+    part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # one rank's share, timed alone
+    for _ in range(3):
+        L.mla_decode_partial(one_args, stream)
+    torch.cuda.synchronize()
+    e1, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e1.record(stream)
+    for _ in range(args.steps):
+        L.mla_decode_partial(one_args, stream)
+    e2.record(stream)
+    torch.cuda.synchronize()
+    share_us = e1.elapsed_time(e2) / args.steps * 1e3
+
+    us = ms_step * 1e3
+    tflops = work["total_flops"] / (us * 1e-6) / 1e12
+    kv_gbs = work["kv_bytes"] / (us * 1e-6) / 1e9
+    t_roof = max(work["total_bytes"] / (HBM_PEAK_GBS * 1e9),
+                 work["total_flops"] / (MFMA_PEAK_TFLOPS[sp.dtype] * 1e12))
+    bound_step = ("hbm" if work["total_bytes"] / (HBM_PEAK_GBS * 1e9) >=
+                  work["total_flops"] / (MFMA_PEAK_TFLOPS[sp.dtype] * 1e12) else "mfma")
+    part_bytes = work["partial_bytes"]
+    achieved = part_bytes / (part_ms * 1e-3) / 1e9
+    wl = f"config{sp.wid}:{sp.name}"
+    traffic = traffic_from_profile(wl)
+    res = {
+        "metric": METRIC,
+        "value": round(us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": sp.dtype,
+        "data": "synthetic (seeded; DeepSeek-shaped MLA: d_c=512, d_R=64, random weights)",
+        "config": {"workload": wl, "B": sp.B, "H": sp.H, "q_len": sp.S,
+                   "L": list(sp.lengths), "block_size": sp.block_size, "parts": sp.parts,
+                   "part_out_dtype": sp.part_out_dtype, "part_lse_dtype": sp.part_lse_dtype},
+        "tflops": round(tflops, 2),
+        "kv_gbs": round(kv_gbs, 1),
+        "step_roofline": {"bound": bound_step, "t_roof_us": round(t_roof * 1e6, 2),
+                          "frac": round(t_roof * 1e6 / us, 4),
+                          "algorithmic_bytes": work["total_bytes"],
+                          "algorithmic_flops": work["total_flops"]},
+        "roofline": {"kernel": "partial_mfma_kernel (mla_decode_partial, all parts)",
+                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": part_bytes,
+                     "avg_launch_us": round(part_ms * 1e3, 2),
+                     "mfma_tflops": round(work["attn_flops"] / (part_ms * 1e-3) / 1e12, 1)},
+        "one_rank_share_us": round(share_us, 2),
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * mla_decode.h -- C ABI of the absorbed split-KV MLA decode library
+ * (libmla_decode.so, HIP kernels for gfx950 / MI355X).
+ *
+ * One decode step of Multi-head Latent Attention over a latent KV cache:
+ *
+ *   q_lat = W_UK[h] . q_nope                      mla_q_absorb
+ *   (o_p, lse_p) = attention over part p's keys   mla_decode_partial
+ *   o = LSE merge of the parts (+ a local part)   mla_lse_combine
+ *   out = o . W_UV[h]  -> [T][H*128]               mla_vup
+ *
+ * The operations follow the "DCP decode streams / V-up" study page (vLLM
+ * Ascend PR notes): a decode step splits the keys into parts along the
+ * sequence (decode context parallelism), each part returns a partial output
+ * and its log-sum-exp (background section), the partials are merged by LSE
+ * into the exact full-sequence softmax (combine step, "local_output /
+ * local_lse" read without packing), and the batch-major latent result goes
+ * through one transpose-free batched V-up (V-up fusion section). The latent
+ * row layout (c_KV 512 + k_R 64 = 576 values per token, shared by every head)
+ * and the paged block sizes follow the "MLA multi-GPU sharding" page
+ * (latent-vector and --block-size sections).
+ *
+ * Fixed dimensions: d_c = 512, d_R = 64, d_nope = d_v = 128.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless stated otherwise. The caller owns
+ *    every buffer; the library allocates nothing in these calls, keeps no
+ *    pointer after return, and does not synchronise the host.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream). Calls contain no host sync, no event creation and no
+ *    allocation, so they may be recorded into a HIP graph.
+ *  - Host-side validation happens before any launch; on error nothing is
+ *    enqueued and a negative MLA_ERR_* code is returned. A failed launch
+ *    returns MLA_ERR_HIP. Device faults surface at the caller's next sync.
+ *  - Outputs must not overlap inputs (checked where the extents are known:
+ *    MLA_ERR_ALIAS).
+ *  - Results are bitwise reproducible for identical inputs and arguments
+ *    (fixed reduction orders, no floating-point atomics).
+ *  - Accumulation is fp32; results are rounded to nearest-even into the
+ *    output dtype.
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_D_C 512
+#define MLA_D_R 64
+#define MLA_D_ROW 576
+#define MLA_D_NOPE 128
+#define MLA_D_V 128
+
+/* element types */
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_F16 = 2 } mla_dtype;
+
+/* key visibility inside a part's range [start, end):
+ *  NONE          every key of the range is visible (the history segment).
+ *  CAUSAL_WINDOW bottom-right aligned window: query s (0 <= s < S) sees the
+ *                range's keys at offsets j <= (end - start) - S + s. With a
+ *                range holding the S current-chunk tokens this is the MTP
+ *                current-window mask (study page: the CURRENT call with its
+ *                attn_mask). */
+typedef enum { MLA_MASK_NONE = 0, MLA_MASK_CAUSAL_WINDOW = 1 } mla_mask;
+
+/* status codes */
+enum {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL                       */
+  MLA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent           */
+  MLA_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination   */
+  MLA_ERR_RANGE = -4,       /* an argument value is out of its documented range */
+  MLA_ERR_WORKSPACE = -5,   /* workspace missing or smaller than required       */
+  MLA_ERR_UNSUPPORTED = -6, /* valid but not implemented (e.g. S > 64)          */
+  MLA_ERR_HIP = -7,         /* a HIP runtime call or kernel launch failed       */
+  MLA_ERR_ALIAS = -8        /* an output overlaps an input                      */
+};
+
+/* flags for mla_partial_args.flags */
+#define MLA_FLAG_FORCE_SIMPLE 1u /* use the plain VALU kernel (testing aid) */
+
+/*
+ * Arguments of mla_decode_partial.
+ *
+ * Queries: T = B*S query tokens, t = b*S + s.
+ *   q_lat  [T][H][512]  absorbed query (q_dtype)
+ *   q_rope [T][H][64]   rotary query (q_dtype, already rotated)
+ * Cache (kv_dtype == q_dtype), one row = c_KV (512) || k_R (64):
+ *   paged      (block_size > 0): kv [num_blocks][block_size][576];
+ *              block_table int32 [B][max_blocks]: logical token j of
+ *              sequence b sits in row block_table[b][j / block_size],
+ *              slot j % block_size.
+ *   contiguous (block_size == 0, block_table == NULL, the study page's
+ *              current-chunk convention): kv [B][kv_seq_stride][576].
+ * Parts: P >= 1 parts; range_start/range_end int32 [P][B] (DEVICE arrays)
+ *   give part p's logical key range [start, end) of sequence b. An empty
+ *   range yields out = 0 and lse = -inf. A range outside
+ *   [0, capacity] (capacity = max_blocks*block_size or kv_seq_stride) or a
+ *   referenced block id outside [0, num_blocks) is detected on the device:
+ *   that (part, sequence)'s out and lse are filled with NaN and nothing is
+ *   read out of bounds.
+ * Score: s_j = scale * (q_lat . c_j + q_rope . kR_j). lse is the natural
+ *   log-sum-exp of the scaled scores of the visible keys.
+ * Outputs:
+ *   out [P][T][H][512] (out_dtype): sum_j softmax_j * c_j over the part
+ *   lse [P][T][H]      (lse_dtype)
+ * Workspace: `workspace_bytes` >= mla_decode_partial_workspace_size(args)
+ *   bytes of device memory (may be 0 bytes / NULL when the size is 0). It is
+ *   exclusive to the call until the stream has passed it; two calls that
+ *   share a workspace must be ordered on one stream (or by events).
+ * num_splits: 0 = automatic; otherwise each (part, sequence) range is cut
+ *   into at most this many sub-ranges that are merged inside the call.
+ */
+typedef struct mla_partial_args {
+  const void* q_lat;
+  const void* q_rope;
+  int q_dtype;
+  int B, S, H;
+  const void* kv;
+  int kv_dtype;
+  int block_size;
+  const int32_t* block_table;
+  int max_blocks;
+  int num_blocks;
+  int kv_seq_stride;
+  int P;
+  const int32_t* range_start;
+  const int32_t* range_end;
+  int mask;
+  float scale;
+  void* out;
+  int out_dtype;
+  void* lse;
+  int lse_dtype;
+  void* workspace;
+  size_t workspace_bytes;
+  int num_splits;
+  unsigned flags;
+} mla_partial_args;
+
+/* Bytes of device workspace mla_decode_partial needs for these arguments
+ * (a pure function of the sizes, dtypes and flags; no device access).
+ * Returns (size_t)-1 for invalid arguments. */
+size_t mla_decode_partial_workspace_size(const mla_partial_args* a);
+
+/* Split-KV partial attention: for every part p, query token t and head h,
+ * the softmax-weighted latent sum and LSE over p's visible keys (study page:
+ * the HISTORY and CURRENT attention calls, each returning output + LSE). */
+int mla_decode_partial(const mla_partial_args* a, void* stream);
+
+/* q absorption: q_lat[t][h][c] = sum_j W_UK[h][c][j] * q_nope[t][h][j].
+ *   q_nope [T][H][128], w_uk [H][512][128], q_lat [T][H][512], all `dtype`.
+ * (Not written out on the pages; it is the regrouping that lets the latent
+ * cache serve as every head's key, see the K3 page section 2.1.) */
+int mla_q_absorb(const void* q_nope, const void* w_uk, void* q_lat, int T, int H,
+                 int dtype, void* stream);
+
+/* LSE combine (study page: the combine that reads the received history
+ * shards plus the local current part directly, without packing):
+ *   m = max_i lse_i, w_i = exp(lse_i - m),
+ *   out = sum_i w_i o_i / sum_i w_i, lse_out = m + ln sum_i w_i,
+ * parts in index order, the local part last. Parts with lse = -inf weigh 0;
+ * if all are empty, out = 0 and lse_out = -inf.
+ *   parts_out [P][T][H][512] (part_dtype), parts_lse [P][T][H] (lse_dtype),
+ *   local_out [T][H][512] / local_lse [T][H]: both NULL or both set (same
+ *   dtypes as the parts); P may be 0 when a local part is given.
+ *   out [T][H][512] (out_dtype); lse_out fp32 [T][H] or NULL. */
+int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int part_dtype,
+                    int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
+                    void* out, int out_dtype, float* lse_out, void* stream);
+
+/* V-up on the batch-major latent, transpose-free (study page, V-up fusion):
+ *   out[t][h][v] = sum_c x[t][h][c] * W_UV[h][c][v]
+ *   x [T][H][512], w_uv [H][512][128], out [T][H][128] == [T][H*128]. */
+int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype, void* stream);
+
+/* Human-readable text for a status code (static string, never NULL). */
+const char* mla_status_string(int status);
+
+/* Library ABI version (this header: 1). */
+int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

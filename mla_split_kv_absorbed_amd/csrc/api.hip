@@ -1,0 +1,229 @@
+// C ABI of libmla_decode.so: argument validation, workspace sizing, dispatch.
+// Every check happens on the host before any launch; on error nothing is
+// enqueued.
+#include <limits.h>
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace mla;
+
+namespace {
+
+bool valid_dtype(int d) { return d == MLA_F32 || d == MLA_BF16 || d == MLA_F16; }
+
+struct Extent {
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(Extent a, Extent b) {
+  if (!a.p || !b.p || a.bytes == 0 || b.bytes == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+bool any_overlap(const Extent* outs, int no, const Extent* ins, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+  }
+  return false;
+}
+
+bool use_mfma(const mla_partial_args* a) {
+  return !(a->flags & MLA_FLAG_FORCE_SIMPLE) &&
+         mfma_path_supported(a->q_dtype, a->H, a->block_size);
+}
+
+size_t partial_ws_bytes(const mla_partial_args* a) {
+  if (!use_mfma(a)) return 0;
+  return mfma_workspace_bytes(a->B, a->S, a->H, a->P, a->num_splits);
+}
+
+// Validation without the workspace check; returns MLA_OK or an error code.
+int check_partial_args(const mla_partial_args* a) {
+  if (!a) return MLA_ERR_NULL;
+  if (!a->q_lat || !a->q_rope || !a->kv || !a->range_start || !a->range_end || !a->out ||
+      !a->lse)
+    return MLA_ERR_NULL;
+  if (a->block_size > 0 && !a->block_table) return MLA_ERR_NULL;
+  if (!valid_dtype(a->q_dtype) || !valid_dtype(a->kv_dtype) || !valid_dtype(a->out_dtype) ||
+      !valid_dtype(a->lse_dtype))
+    return MLA_ERR_DTYPE;
+  if (a->q_dtype != a->kv_dtype) return MLA_ERR_DTYPE;
+  if (a->B < 1 || a->S < 1 || a->H < 1 || a->P < 1) return MLA_ERR_SHAPE;
+  if (a->S > 64 || a->H > 65535) return MLA_ERR_UNSUPPORTED;
+  if ((long long)a->P * a->B * a->S > INT_MAX / 8) return MLA_ERR_SHAPE;
+  if (a->block_size < 0) return MLA_ERR_SHAPE;
+  if (a->block_size > 0) {
+    if (a->max_blocks < 1 || a->num_blocks < 1) return MLA_ERR_SHAPE;
+    if ((long long)a->max_blocks * a->block_size > INT_MAX) return MLA_ERR_SHAPE;
+  } else {
+    if (a->block_table) return MLA_ERR_SHAPE;
+    if (a->kv_seq_stride < 1) return MLA_ERR_SHAPE;
+  }
+  if (a->mask != MLA_MASK_NONE && a->mask != MLA_MASK_CAUSAL_WINDOW) return MLA_ERR_RANGE;
+  if (!isfinite(a->scale)) return MLA_ERR_RANGE;
+  if (a->num_splits < 0 || a->num_splits > 4096) return MLA_ERR_RANGE;
+  if (a->flags & ~MLA_FLAG_FORCE_SIMPLE) return MLA_ERR_RANGE;
+  return MLA_OK;
+}
+
+int check_partial_alias(const mla_partial_args* a, size_t ws) {
+  const size_t T = (size_t)a->B * a->S, H = a->H, P = a->P;
+  const size_t e = elem_bytes(a->q_dtype);
+  const size_t kv_rows = a->block_size > 0 ? (size_t)a->num_blocks * a->block_size
+                                           : (size_t)a->B * a->kv_seq_stride;
+  Extent ins[6] = {{a->q_lat, T * H * kDc * e},
+                   {a->q_rope, T * H * kDr * e},
+                   {a->kv, kv_rows * kRow * e},
+                   {a->block_table, a->block_table ? (size_t)a->B * a->max_blocks * 4 : 0},
+                   {a->range_start, P * a->B * 4},
+                   {a->range_end, P * a->B * 4}};
+  Extent outs[3] = {{a->out, P * T * H * kDc * elem_bytes(a->out_dtype)},
+                    {a->lse, P * T * H * elem_bytes(a->lse_dtype)},
+                    {a->workspace, ws}};
+  return any_overlap(outs, 3, ins, 6) ? MLA_ERR_ALIAS : MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mla_abi_version(void) { return 1; }
+
+const char* mla_status_string(int s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_NULL: return "MLA_ERR_NULL: a required pointer is NULL";
+    case MLA_ERR_SHAPE: return "MLA_ERR_SHAPE: a size is out of range or inconsistent";
+    case MLA_ERR_DTYPE: return "MLA_ERR_DTYPE: unknown or unsupported dtype combination";
+    case MLA_ERR_RANGE: return "MLA_ERR_RANGE: an argument value is out of its documented range";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: valid but not implemented";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case MLA_ERR_ALIAS: return "MLA_ERR_ALIAS: an output overlaps an input";
+    default: return "unknown status";
+  }
+}
+
+size_t mla_decode_partial_workspace_size(const mla_partial_args* a) {
+  if (check_partial_args(a) != MLA_OK) return (size_t)-1;
+  return partial_ws_bytes(a);
+}
+
+int mla_decode_partial(const mla_partial_args* a, void* stream) {
+  int st = check_partial_args(a);
+  if (st != MLA_OK) return st;
+  const size_t need = partial_ws_bytes(a);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  st = check_partial_alias(a, need > 0 ? a->workspace_bytes : 0);
+  if (st != MLA_OK) return st;
+
+  PartialParams pp;
+  memset(&pp, 0, sizeof(pp));
+  pp.q_lat = a->q_lat;
+  pp.q_rope = a->q_rope;
+  pp.kv = a->kv;
+  pp.block_table = a->block_table;
+  pp.range_start = a->range_start;
+  pp.range_end = a->range_end;
+  pp.out = a->out;
+  pp.lse = a->lse;
+  pp.B = a->B;
+  pp.S = a->S;
+  pp.H = a->H;
+  pp.P = a->P;
+  pp.block_size = a->block_size;
+  pp.max_blocks = a->max_blocks;
+  pp.num_blocks = a->num_blocks;
+  pp.kv_seq_stride = a->kv_seq_stride;
+  pp.mask = a->mask;
+  pp.out_dtype = a->out_dtype;
+  pp.lse_dtype = a->lse_dtype;
+  pp.num_splits = a->num_splits;
+  pp.scale = a->scale;
+  pp.capacity = a->block_size > 0 ? (long long)a->max_blocks * a->block_size
+                                  : (long long)a->kv_seq_stride;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (use_mfma(a)) {
+    pp.ws_out = (float*)a->workspace;  // workspace base; the launcher lays it out
+    pp.max_chunks = (int)mfma_max_chunks(a->B, a->S, a->P, a->num_splits);
+    e = launch_partial_mfma(pp, a->q_dtype, s);
+  } else {
+    e = launch_partial_simple(pp, a->q_dtype, s);
+  }
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int part_dtype,
+                    int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
+                    void* out, int out_dtype, float* lse_out, void* stream) {
+  if (!out) return MLA_ERR_NULL;
+  if ((local_out == nullptr) != (local_lse == nullptr)) return MLA_ERR_NULL;
+  if (P > 0 && (!parts_out || !parts_lse)) return MLA_ERR_NULL;
+  if (!valid_dtype(part_dtype) || !valid_dtype(lse_dtype) || !valid_dtype(out_dtype))
+    return MLA_ERR_DTYPE;
+  if (P < 0 || T < 1 || H < 1) return MLA_ERR_SHAPE;
+  if (P + (local_out ? 1 : 0) < 1) return MLA_ERR_SHAPE;
+  const size_t rows = (size_t)T * H;
+  if ((rows + 3) / 4 > (size_t)INT_MAX) return MLA_ERR_SHAPE;
+  const size_t pe = elem_bytes(part_dtype), le = elem_bytes(lse_dtype);
+  Extent ins[4] = {{parts_out, (size_t)P * rows * kDc * pe},
+                   {parts_lse, (size_t)P * rows * le},
+                   {local_out, local_out ? rows * kDc * pe : 0},
+                   {local_lse, local_lse ? rows * le : 0}};
+  Extent outs[2] = {{out, rows * kDc * elem_bytes(out_dtype)},
+                    {lse_out, lse_out ? rows * 4 : 0}};
+  if (any_overlap(outs, 2, ins, 4)) return MLA_ERR_ALIAS;
+  CombineParams c;
+  c.parts_out = parts_out;
+  c.parts_lse = parts_lse;
+  c.local_out = local_out;
+  c.local_lse = local_lse;
+  c.out = out;
+  c.lse_out = lse_out;
+  c.P = P;
+  c.T = T;
+  c.H = H;
+  c.part_dtype = part_dtype;
+  c.lse_dtype = lse_dtype;
+  c.out_dtype = out_dtype;
+  return launch_combine(c, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype, void* stream) {
+  if (!x || !w_uv || !out) return MLA_ERR_NULL;
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (T < 1 || H < 1 || H > 65535) return MLA_ERR_SHAPE;
+  const size_t e = elem_bytes(dtype);
+  Extent ins[2] = {{x, (size_t)T * H * kDc * e}, {w_uv, (size_t)H * kDc * kDv * e}};
+  Extent outs[1] = {{out, (size_t)T * H * kDv * e}};
+  if (any_overlap(outs, 1, ins, 2)) return MLA_ERR_ALIAS;
+  return launch_vup_simple(x, w_uv, out, T, H, dtype, (hipStream_t)stream) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+int mla_q_absorb(const void* q_nope, const void* w_uk, void* q_lat, int T, int H, int dtype,
+                 void* stream) {
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_NULL;
+  if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;
+  if (T < 1 || H < 1 || H > 65535) return MLA_ERR_SHAPE;
+  const size_t e = elem_bytes(dtype);
+  Extent ins[2] = {{q_nope, (size_t)T * H * kDn * e}, {w_uk, (size_t)H * kDc * kDn * e}};
+  Extent outs[1] = {{q_lat, (size_t)T * H * kDc * e}};
+  if (any_overlap(outs, 1, ins, 2)) return MLA_ERR_ALIAS;
+  return launch_absorb_simple(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream) ==
+                 hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+}  // extern "C"

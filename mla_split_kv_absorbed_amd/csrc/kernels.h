@@ -1,0 +1,34 @@
+// Launchers of the library's kernels (internal; the public ABI is mla_decode.h).
+#pragma once
+
+#include "common.h"
+
+namespace mla {
+
+struct CombineParams {
+  const void* parts_out;
+  const void* parts_lse;
+  const void* local_out;
+  const void* local_lse;
+  void* out;
+  float* lse_out;
+  int P, T, H;
+  int part_dtype, lse_dtype, out_dtype;
+};
+
+hipError_t launch_partial_simple(const PartialParams& pp, int dtype, hipStream_t st);
+// MFMA path: q/kv dtype bf16 or f16, H % 128 == 0, block_size % 32 == 0 (or contiguous).
+bool mfma_path_supported(int dtype, int H, int block_size);
+hipError_t launch_partial_mfma(const PartialParams& pp, int dtype, hipStream_t st);
+// Upper bound on split sub-ranges ("slots") an MFMA-path call may write.
+size_t mfma_max_slots(int B, int S, int P, int num_splits);
+size_t mfma_max_chunks(int B, int S, int P, int num_splits);
+size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits);
+
+hipError_t launch_combine(const CombineParams& c, hipStream_t st);
+hipError_t launch_vup_simple(const void* x, const void* w, void* out, int T, int H, int dt,
+                             hipStream_t st);
+hipError_t launch_absorb_simple(const void* qn, const void* w, void* ql, int T, int H, int dt,
+                                hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,598 @@
+// Split-KV partial attention on CDNA4 matrix cores (bf16 / fp16 in, fp32
+// accumulate), the hot kernel of the decode step.
+//
+// Work decomposition. One workgroup owns one query token of one (part,
+// sequence) range -- or one sub-range ("chunk") of it -- for 128 heads. All
+// 128 heads share the latent cache, so each 576-wide key row is read from HBM
+// once and used by every head: the head-batched products S^T = K . Q^T and
+// O^T += C^T . P^T are real dense contractions (M = 32 tokens or 32 latent
+// columns, N = 32 heads per wave, K = 576 dims or 32 tokens).
+//
+// Data flow per 32-token tile (one LDS stage of 32 x 576 x 2 B = 36 KB):
+//   HBM --buffer_load_dwordx4 ... lds--> LDS ring (4 stages, no VGPRs used)
+//   LDS --ds_read_b128--> key operand of S^T = K Q^T (32x32x16 MFMA, Q in VGPRs)
+//   online softmax in registers (each lane holds 16 tokens of one head)
+//   LDS --ds_read_b64_tr_b16--> transposed value operand of O^T += C^T P^T
+// LDS layout of a stage is chunk-major: the 16-byte chunk c (8 values) of
+// key row r sits at slot c*32 + (r ^ 4*(c&1)). One LDS-direct load covers
+// two chunk columns for all 32 rows, so every lane's source offset is one
+// register plus a scalar per load; key-operand reads are 512 contiguous bytes
+// per half wave, and the transposed reads of the value operand touch two
+// disjoint 64-byte bank ranges per 16 lanes (the XOR with c&1).
+//
+// Each wave owns 32 heads: Q^T for them stays in 144 VGPRs, the fp32 output
+// O^T (512 x 32) in 256 accumulation registers. Softmax uses a lazily updated
+// reference maximum (rescale only when a head's maximum grows by more than
+// 2^8), which keeps every probability <= 256 and the final normalisation
+// exact.
+//
+// Ranges that need splitting (few sequences, long ranges) are cut into
+// chunks; chunk results go to a fp32 workspace and a second kernel merges
+// them by LSE in a fixed order.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef short shortx8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;                      // 4 x 32 heads = 128 heads per group
+constexpr int kHeadsWave = 32;
+constexpr int kHeadsGroup = kWaves * kHeadsWave;
+constexpr int kStages = 4;
+constexpr int kRowBytes = kRow * 2;            // 1152
+constexpr int kChunksRow = kRowBytes / 16;     // 72
+constexpr int kStageBytes = kTile * kRowBytes; // 36864
+constexpr int kLoadsWave = kStageBytes / 16 / 64 / kWaves;  // 9
+constexpr int kKSteps = kRow / 16;             // 36
+constexpr int kDTiles = kDc / 32;              // 16
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRescaleThresh = 8.0f;         // log2 units
+
+static_assert(kLoadsWave * 64 * 16 * kWaves == kStageBytes, "stage load split");
+
+
+__device__ __forceinline__ void wait_vm(int n_after) {
+  // vmcnt(9 * n_after); expcnt / lgkmcnt left unconstrained
+  if (n_after >= 2) __builtin_amdgcn_s_waitcnt(0x4F72);       // vmcnt(18)
+  else if (n_after == 1) __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
+  else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+}
+
+template <typename T> struct MT;
+template <> struct MT<bf16> {
+  typedef bf16x8 v8;
+  static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct MT<f16> {
+  typedef f16x8 v8;
+  static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// the plan: tiles, chunks and split slots of one call, computed in-kernel
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int range_tiles(int st, int en) {
+  return en > st ? (en - 1) / kTile - st / kTile + 1 : 0;
+}
+
+struct Unit {
+  int st, en;
+  bool bad;
+  int nt;
+};
+
+__device__ __forceinline__ Unit load_unit(const PartialParams& pp, int u) {
+  Unit x;
+  x.st = pp.range_start[u];
+  x.en = pp.range_end[u];
+  x.bad = x.st < 0 || x.en < x.st || (long long)x.en > pp.capacity;
+  x.nt = x.bad ? 0 : range_tiles(x.st, x.en);
+  return x;
+}
+
+__device__ __forceinline__ int unit_chunks(int nt, int c, int hint) {
+  if (hint > 0) return min(hint, max(1, nt));
+  return max(1, (nt + c - 1) / c);
+}
+
+// block-wide exclusive scan of one int per thread (256 threads)
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int x = tid >= o ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += x;
+    __syncthreads();
+  }
+  total = sh[255];
+  int r = sh[tid] - v;
+  __syncthreads();
+  return r;
+}
+
+struct Plan {
+  int chunk_tiles;   // c
+  int nchunks;       // total chunks
+  int nsplit_units;  // units cut into more than one chunk
+};
+
+// Computes the plan; if `want` >= 0, also finds chunk `want`:
+// found = {unit, first tile, end tile, slot (-1 = direct), chunk index in unit}
+struct Found {
+  int u, tb, te, slot, nsplit, split_idx;
+};
+
+__device__ Plan make_plan(const PartialParams& pp, int want, Found* found, int* sh) {
+  const int tid = threadIdx.x;
+  const int U = pp.P * pp.B;
+  const int per = (U + 255) / 256;
+  const int u0 = min(U, tid * per), u1 = min(U, u0 + per);
+  long long my_tiles = 0;
+  for (int u = u0; u < u1; ++u) my_tiles += load_unit(pp, u).nt;
+  // total tiles (fits in int for any addressable cache)
+  int total;
+  block_excl_scan((int)my_tiles, sh, total);
+  Plan pl;
+  const long long want_groups = kTargetGroups;
+  long long c = ((long long)total * pp.S + want_groups - 1) / want_groups;
+  pl.chunk_tiles = (int)max((long long)kMinChunkTiles, c);
+  int my_chunks = 0, my_slots = 0, my_splits = 0;
+  for (int u = u0; u < u1; ++u) {
+    const Unit x = load_unit(pp, u);
+    const int n = unit_chunks(x.nt, pl.chunk_tiles, pp.num_splits);
+    my_chunks += n;
+    if (n > 1) {
+      my_slots += n;
+      my_splits += 1;
+    }
+  }
+  int tot_chunks, tot_slots, tot_splits;
+  int cbase = block_excl_scan(my_chunks, sh, tot_chunks);
+  int sbase = block_excl_scan(my_slots, sh, tot_slots);
+  int pbase = block_excl_scan(my_splits, sh, tot_splits);
+  pl.nchunks = tot_chunks;
+  pl.nsplit_units = tot_splits;
+  if (want >= 0 && want >= cbase && want < cbase + my_chunks) {
+    int off = cbase, soff = sbase, poff = pbase;
+    for (int u = u0; u < u1; ++u) {
+      const Unit x = load_unit(pp, u);
+      const int n = unit_chunks(x.nt, pl.chunk_tiles, pp.num_splits);
+      if (want < off + n) {
+        const int i = want - off;
+        found->u = u;
+        found->tb = (int)((long long)i * x.nt / n);
+        found->te = (int)((long long)(i + 1) * x.nt / n);
+        found->slot = n > 1 ? soff + i : -1;
+        found->nsplit = n;
+        found->split_idx = n > 1 ? poff : -1;
+        break;
+      }
+      off += n;
+      if (n > 1) {
+        soff += n;
+        poff += 1;
+      }
+    }
+  }
+  return pl;
+}
+
+// workspace layout: [count | pad 256][split descriptors U x int4][lse][out]
+struct WsLayout {
+  size_t desc_off, lse_off, out_off, total;
+};
+
+__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+__host__ __device__ inline size_t slots_bound(int B, int S, int P, int hint) {
+  const size_t U = (size_t)P * B;
+  if (hint == 1) return 0;
+  if (hint > 1) return U * hint;
+  return (2 * kTargetGroups + S - 1) / S + 1;
+}
+
+__host__ __device__ inline WsLayout ws_layout(int B, int S, int H, int P, int hint) {
+  WsLayout w;
+  const size_t U = (size_t)P * B;
+  const size_t rows = slots_bound(B, S, P, hint) * S * H;
+  w.desc_off = 256;
+  w.lse_off = align256(w.desc_off + U * 16);
+  w.out_off = align256(w.lse_off + rows * 4);
+  w.total = align256(w.out_off + rows * kDc * 4);
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// the main kernel
+// ---------------------------------------------------------------------------
+
+struct MfmaParams {
+  PartialParams pp;
+  int* ws_count;
+  intx4* ws_desc;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
+  const PartialParams& pp = mp.pp;
+  typedef typename MT<T>::v8 v8;
+  // one LDS object per stage, so the compiler can tell a stage's reads from
+  // the loads still landing in the other stages
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
+  auto stage_ptr = [&](int st) -> char* {
+    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
+  };
+  __shared__ int sh_scan[256];
+  __shared__ Found sh_found;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = pp.S;
+
+  // blockIdx -> (chunk, query): the S queries of one chunk sit 8 ids apart,
+  // i.e. on the same XCD, so their shared key tiles meet in one L2
+  int chunk, s;
+  if (S == 1) {
+    chunk = blockIdx.x;
+    s = 0;
+  } else {
+    const int grp = blockIdx.x / (8 * S), r = blockIdx.x % (8 * S);
+    chunk = grp * 8 + (r & 7);
+    s = r >> 3;
+  }
+  if (tid == 0) sh_found.u = -1;
+  __syncthreads();
+  const Plan pl = make_plan(pp, chunk, &sh_found, sh_scan);
+  __syncthreads();
+  if (blockIdx.x == 0 && tid == 0) *mp.ws_count = pl.nsplit_units;
+  Found fd;
+  fd.u = __builtin_amdgcn_readfirstlane(sh_found.u);
+  if (fd.u < 0) return;  // grid slack beyond the plan's chunks
+  fd.tb = __builtin_amdgcn_readfirstlane(sh_found.tb);
+  fd.te = __builtin_amdgcn_readfirstlane(sh_found.te);
+  fd.slot = __builtin_amdgcn_readfirstlane(sh_found.slot);
+  fd.nsplit = __builtin_amdgcn_readfirstlane(sh_found.nsplit);
+  fd.split_idx = __builtin_amdgcn_readfirstlane(sh_found.split_idx);
+
+  const int p = fd.u / pp.B, b = fd.u % pp.B;
+  const int t = b * S + s;
+  const int Tq = pp.B * S;
+  const int st = pp.range_start[fd.u];
+  const int en = pp.range_end[fd.u];
+  const bool unit_bad = st < 0 || en < st || (long long)en > pp.capacity;
+  int vend = en;
+  if (pp.mask == MLA_MASK_CAUSAL_WINDOW) vend = min(en, en - S + s + 1);
+  // chunk 0 of a split range records where its chunks' results live
+  if (fd.split_idx >= 0 && fd.tb == 0 && s == 0 && tid == 0)
+    mp.ws_desc[fd.split_idx] = intx4{fd.u, fd.slot, fd.nsplit, 0};
+
+  // ---- per-lane constants -------------------------------------------------
+  const int hi = lane >> 5;          // 0/1: which half of a 16-wide k step
+  const int r32 = lane & 31;         // key row (QK) / head column
+  const int head = wave * kHeadsWave + r32;
+  // key operand: row r32, chunk 2k + hi  -> k*1024 + qk_lane
+  const int qk_lane = hi * 512 + ((r32 ^ (4 * hi)) << 4);
+  // value operand (transposed read): chunk 4d + 2(g16&1) + x, row 16kk + 8e + 4h + q
+  const int j16 = lane & 15, g16 = lane >> 4, q4 = j16 >> 2, xx = (j16 & 3) >> 1;
+  const int pv_lane = (2 * (g16 & 1) + xx) * 512 + ((4 * (hi ^ xx) + q4) << 4) + ((j16 & 1) << 3);
+  // LDS-direct loads: load g covers chunks 2g, 2g+1; lane -> (row, chunk parity)
+  const int ld_lane = ((r32 ^ (4 * hi)) * kRowBytes) + hi * 16;
+
+  // ---- Q^T for this wave's 32 heads, in registers -------------------------
+  v8 q[kKSteps];
+  {
+    const T* ql = (const T*)pp.q_lat + ((size_t)t * pp.H + head) * kDc;
+    const T* qr = (const T*)pp.q_rope + ((size_t)t * pp.H + head) * kDr;
+#pragma unroll
+    for (int k = 0; k < kKSteps; ++k) {
+      const int d = k * 16 + hi * 8;
+      q[k] = d < kDc ? *(const v8*)(ql + d) : *(const v8*)(qr + (d - kDc));
+    }
+  }
+
+  floatx16 o[kDTiles];
+#pragma unroll
+  for (int i = 0; i < kDTiles; ++i)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) o[i][j] = 0.f;
+  float m_ref = -INFINITY, l_part = 0.f, l_round = 0.f;
+  bool bad = unit_bad;
+  const float sl2 = pp.scale * kLog2e;
+
+  const int tb = fd.tb, te = unit_bad ? fd.tb : fd.te;
+  const int st_tile = st / kTile;
+  const char* kvb = (const char*)pp.kv;
+
+  // tile -> (first token, token count, buffer resource)
+  auto tile_tok0 = [&](int j) { return j == 0 ? st : (st_tile + j) * kTile; };
+  auto issue = [&](int j, int stage) {
+    const int tok0 = tile_tok0(j);
+    const int tok1 = min(en, (st_tile + j + 1) * kTile);
+    const char* base;
+    int nrows = tok1 - tok0;
+    if (pp.block_size > 0) {
+      const int id = ((const __attribute__((address_space(4))) int*)
+                          pp.block_table)[(size_t)b * pp.max_blocks + tok0 / pp.block_size];
+      if (id < 0 || id >= pp.num_blocks) {
+        bad = true;
+        nrows = 0;
+        base = kvb;
+      } else {
+        base = kvb + ((size_t)id * pp.block_size + (tok0 % pp.block_size)) * kRowBytes;
+      }
+    } else {
+      base = kvb + ((size_t)b * pp.kv_seq_stride + tok0) * kRowBytes;
+    }
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrows * kRowBytes, 0x00020000);
+    char* dst = stage_ptr(stage) + wave * kLoadsWave * 1024;
+#pragma unroll
+    for (int i = 0; i < kLoadsWave; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + i * 1024), 16, ld_lane,
+                                               (wave * kLoadsWave + i) * 32, 0, 0);
+  };
+
+  // ---- prologue: 3 tiles in flight -----------------------------------------
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i)
+    if (tb + i < te) issue(tb + i, i);
+
+  auto step = [&](int j, int stage) {
+    wait_vm(min(2, te - 1 - j));
+    __syncthreads();
+    if (j + kStages - 1 < te) issue(j + kStages - 1, (stage + kStages - 1) % kStages);
+    const char* sb = stage_ptr(stage);
+
+    // S^T = K . Q^T over 576 dims; key operands prefetched 4 k-steps ahead,
+    // scheduling fences keep the prefetch window (and register use) bounded
+    floatx16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    v8 kb[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) kb[k] = *(const v8*)(sb + qk_lane + k * 1024);
+#pragma unroll
+    for (int k = 0; k < kKSteps; ++k) {
+      sacc = MT<T>::mfma(kb[k & 3], q[k], sacc);
+      if (k + 4 < kKSteps)
+        kb[k & 3] = *(const v8*)(sb + qk_lane + (k + 4) * 1024);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // mask, scale (log2 domain), running maximum
+    const int tok0 = tile_tok0(j);
+    const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 8 * (i >> 2) + 4 * hi + (i & 3);
+      sacc[i] = row < nvis ? sacc[i] * sl2 : -INFINITY;
+      mloc = fmaxf(mloc, sacc[i]);
+    }
+    const float mt = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+    const bool need = mt > m_ref + kRescaleThresh;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mn = need ? mt : m_ref;
+      const float alpha = need ? (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn))
+                               : 1.f;
+      l_part *= alpha;
+      l_round *= alpha;
+#pragma unroll
+      for (int d = 0; d < kDTiles; ++d) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
+      }
+      m_ref = mn;
+    }
+    v8 pb[2];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      // the output is normalised by the same rounded weights the matrix
+      // product uses; the LSE comes from the unrounded ones
+      const float pf = sacc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[i] - m_ref);
+      const T pt = (T)pf;
+      l_part += pf;
+      l_round += (float)pt;
+      pb[i >> 3][i & 7] = pt;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // O^T += C^T . P^T, C = the tile's 512 latent columns; transposed value
+    // operands prefetched 2 MFMAs ahead
+    auto vload = [&](int n) {
+      const int d = n >> 1, kk = n & 1;
+      const char* a0 = sb + pv_lane + d * 2048 + kk * 256;
+      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)a0);
+      const shortx4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + 128));
+      return __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    v8 vb[3];
+    vb[0] = vload(0);
+    vb[1] = vload(1);
+#pragma unroll
+    for (int n = 0; n < 2 * kDTiles; ++n) {
+      if (n + 2 < 2 * kDTiles) vb[(n + 2) % 3] = vload(n + 2);
+      o[n >> 1] = MT<T>::mfma(vb[n % 3], pb[n & 1], o[n >> 1]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  for (int j = tb; j < te; j += kStages) {
+    step(j, 0);
+    if (j + 1 < te) step(j + 1, 1);
+    if (j + 2 < te) step(j + 2, 2);
+    if (j + 3 < te) step(j + 3, 3);
+  }
+
+  // ---- epilogue -------------------------------------------------------------
+  const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+  const float l_rnd = l_round + __shfl_xor(l_round, 32, 64);
+  float inv, lse;
+  if (bad) {
+    inv = NAN;
+    lse = NAN;
+  } else if (l_tot > 0.f) {
+    inv = 1.f / l_rnd;
+    lse = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+  } else {
+    inv = 0.f;
+    lse = -INFINITY;
+  }
+  const size_t row = fd.slot < 0 ? ((size_t)p * Tq + t) * pp.H + head
+                                 : ((size_t)fd.slot * S + s) * pp.H + head;
+  if (fd.slot < 0) {
+#pragma unroll
+    for (int d = 0; d < kDTiles; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const size_t col = (size_t)d * 32 + 8 * g + 4 * hi;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          store_any(pp.out, row * kDc + col + i, pp.out_dtype, bad ? NAN : o[d][4 * g + i] * inv);
+      }
+    if (hi == 0) store_any(pp.lse, row, pp.lse_dtype, lse);
+  } else {
+    float* dst = pp.ws_out + row * kDc;
+#pragma unroll
+    for (int d = 0; d < kDTiles; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = d * 32 + 8 * g + 4 * hi;
+        float4 v;
+        v.x = bad ? NAN : o[d][4 * g + 0] * inv;
+        v.y = bad ? NAN : o[d][4 * g + 1] * inv;
+        v.z = bad ? NAN : o[d][4 * g + 2] * inv;
+        v.w = bad ? NAN : o[d][4 * g + 3] * inv;
+        *(float4*)(dst + col) = v;
+      }
+    if (hi == 0) pp.ws_lse[row] = lse;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge of split chunks (fixed order), one wave per (unit, query, head) row
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
+  const PartialParams& pp = mp.pp;
+  const int lane = threadIdx.x & 63;
+  const int n_units = *mp.ws_count;
+  const long long rows = (long long)n_units * pp.S * pp.H;
+  const int Tq = pp.B * pp.S;
+  for (long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
+       r += (long long)gridDim.x * 4) {
+    const int h = (int)(r % pp.H);
+    const int s = (int)((r / pp.H) % pp.S);
+    const int k = (int)(r / ((long long)pp.H * pp.S));
+    const intx4 dsc = mp.ws_desc[k];
+    const int u = dsc[0], slot0 = dsc[1], n = dsc[2];
+    float m = -INFINITY;
+    bool nan_seen = false;
+    for (int i = 0; i < n; ++i) {
+      const float li = pp.ws_lse[((size_t)(slot0 + i) * pp.S + s) * pp.H + h];
+      nan_seen |= isnan(li);
+      m = fmaxf(m, li);
+    }
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float z = 0.f;
+    if (m != -INFINITY && !nan_seen) {
+      for (int i = 0; i < n; ++i) {
+        const size_t wr = ((size_t)(slot0 + i) * pp.S + s) * pp.H + h;
+        const float li = pp.ws_lse[wr];
+        if (li == -INFINITY) continue;
+        const float w = expf(li - m);
+        z += w;
+        const float4* src = (const float4*)(pp.ws_out + wr * kDc + lane * 8);
+        const float4 a = src[0], c = src[1];
+        acc[0] = fmaf(w, a.x, acc[0]);
+        acc[1] = fmaf(w, a.y, acc[1]);
+        acc[2] = fmaf(w, a.z, acc[2]);
+        acc[3] = fmaf(w, a.w, acc[3]);
+        acc[4] = fmaf(w, c.x, acc[4]);
+        acc[5] = fmaf(w, c.y, acc[5]);
+        acc[6] = fmaf(w, c.z, acc[6]);
+        acc[7] = fmaf(w, c.w, acc[7]);
+      }
+    }
+    const int p = u / pp.B, b = u % pp.B;
+    const size_t orow = ((size_t)p * Tq + b * pp.S + s) * pp.H + h;
+    float lse;
+    if (nan_seen) {
+      for (int i = 0; i < 8; ++i) acc[i] = NAN;
+      lse = NAN;
+    } else if (z > 0.f) {
+      const float inv = 1.f / z;
+      for (int i = 0; i < 8; ++i) acc[i] *= inv;
+      lse = m + logf(z);
+    } else {
+      for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+      lse = -INFINITY;
+    }
+    for (int i = 0; i < 8; ++i) store_any(pp.out, orow * kDc + lane * 8 + i, pp.out_dtype, acc[i]);
+    if (lane == 0) store_any(pp.lse, orow, pp.lse_dtype, lse);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+bool mfma_path_supported(int dtype, int H, int block_size) {
+  return (dtype == MLA_BF16 || dtype == MLA_F16) && H == kHeadsGroup &&
+         (block_size == 0 || block_size % kTile == 0);
+}
+
+size_t mfma_max_slots(int B, int S, int P, int hint) { return slots_bound(B, S, P, hint); }
+
+size_t mfma_max_chunks(int B, int S, int P, int hint) {
+  const size_t U = (size_t)P * B;
+  if (hint > 0) return U * hint;
+  return U + (kTargetGroups + S - 1) / S + 1;
+}
+
+size_t mfma_workspace_bytes(int B, int S, int H, int P, int hint) {
+  return ws_layout(B, S, H, P, hint).total;
+}
+
+hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_t st) {
+  MfmaParams mp;
+  mp.pp = pp_in;
+  const WsLayout w = ws_layout(pp_in.B, pp_in.S, pp_in.H, pp_in.P, pp_in.num_splits);
+  char* ws = (char*)pp_in.ws_out;  // base of the workspace
+  mp.ws_count = (int*)ws;
+  mp.ws_desc = (intx4*)(ws + w.desc_off);
+  mp.pp.ws_lse = (float*)(ws + w.lse_off);
+  mp.pp.ws_out = (float*)(ws + w.out_off);
+  const size_t chunks = mfma_max_chunks(pp_in.B, pp_in.S, pp_in.P, pp_in.num_splits);
+  size_t groups = chunks * pp_in.S;
+  if (pp_in.S > 1) groups = (groups + 8 * pp_in.S - 1) / (8 * pp_in.S) * (8 * pp_in.S);
+  dim3 grid((unsigned)groups);
+  if (dtype == MLA_BF16)
+    hipLaunchKernelGGL(partial_mfma_kernel<bf16>, grid, dim3(256), 0, st, mp);
+  else
+    hipLaunchKernelGGL(partial_mfma_kernel<f16>, grid, dim3(256), 0, st, mp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(split_merge_kernel, dim3(kTargetGroups), dim3(256), 0, st, mp);
+  return hipGetLastError();
+}
+
+}  // namespace mla

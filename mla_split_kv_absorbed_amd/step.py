@@ -1,0 +1,117 @@
+"""One absorbed split-KV MLA decode step on the device, as four library calls:
+
+  mla_q_absorb -> mla_decode_partial (history parts [+ current chunk])
+  -> mla_lse_combine -> mla_vup
+
+This module only uploads a workload, allocates the outputs and marshals
+arguments; all arithmetic happens in libmla_decode.so.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib as L
+from .workloads import D_C, D_V, Workload
+
+TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """Storage array (bf16 as uint16 bits) -> device tensor of `dtype`."""
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+class DecodeStep:
+    """Device-resident inputs, outputs and workspace of one decode step."""
+
+    def __init__(self, w: Workload, device="cuda", part_lse_dtype: Optional[str] = None,
+                 num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None):
+        sp = w.spec
+        self.w = w
+        self.dev = torch.device(device)
+        dt = sp.dtype
+        self.dt = TORCH_DT[dt]
+        B, H, S, T, P = sp.B, sp.H, sp.S, w.T, sp.parts
+        self.B, self.H, self.S, self.T, self.P = B, H, S, T, P
+        pdt = TORCH_DT[sp.part_out_dtype]
+        ldt = TORCH_DT[part_lse_dtype or sp.part_lse_dtype]
+        odt = TORCH_DT[sp.out_dtype or dt]
+        dev = self.dev
+
+        self.w_uk = to_device(w.w_uk, dt, dev)
+        self.w_uv = to_device(w.w_uv, dt, dev)
+        self.q_nope = to_device(w.q_nope, dt, dev)
+        self.q_rope = to_device(w.q_rope, dt, dev)
+        self.kv = to_device(w.kv, dt, dev)
+        self.block_table = (torch.from_numpy(w.block_table).to(dev)
+                            if w.block_table is not None else None)
+        self.range_start = torch.from_numpy(w.range_start).to(dev)
+        self.range_end = torch.from_numpy(w.range_end).to(dev)
+        self.q_lat = torch.empty((T, H, D_C), dtype=self.dt, device=dev)
+        self.absorb = q_lat_in is None
+        if q_lat_in is not None:
+            self.q_lat.copy_(to_device(q_lat_in, dt, dev))
+        self.parts_out = torch.empty((P, T, H, D_C), dtype=pdt, device=dev)
+        self.parts_lse = torch.empty((P, T, H), dtype=ldt, device=dev)
+        self.lat = torch.empty((T, H, D_C), dtype=odt, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H, D_V), dtype=self.dt, device=dev)
+
+        kw = dict(B=B, S=S, H=H, scale=sp.scale, num_splits=num_splits, flags=flags)
+        if sp.block_size > 0:
+            kw.update(block_table=self.block_table, block_size=sp.block_size,
+                      num_blocks=w.kv.shape[0])
+        else:
+            kw.update(kv_seq_stride=w.kv.shape[1])
+        self.hist_args = L.partial_args(self.q_lat, self.q_rope, self.kv, self.range_start,
+                                        self.range_end, self.parts_out, self.parts_lse, **kw)
+        ws = L.mla_decode_partial_workspace_size(self.hist_args)
+        self.cur = None
+        if sp.current:
+            self.cur_kv = to_device(w.cur_kv, dt, dev)
+            self.cur_start = torch.zeros((1, B), dtype=torch.int32, device=dev)
+            self.cur_end = torch.full((1, B), S, dtype=torch.int32, device=dev)
+            self.cur_out = torch.empty((T, H, D_C), dtype=pdt, device=dev)
+            self.cur_lse = torch.empty((T, H), dtype=ldt, device=dev)
+            self.cur_args = L.partial_args(self.q_lat, self.q_rope, self.cur_kv, self.cur_start,
+                                           self.cur_end, self.cur_out, self.cur_lse,
+                                           B=B, S=S, H=H, scale=sp.scale, kv_seq_stride=S,
+                                           mask=L.MLA_MASK_CAUSAL_WINDOW, num_splits=num_splits,
+                                           flags=flags)
+            ws = max(ws, L.mla_decode_partial_workspace_size(self.cur_args))
+        self.workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+        for a in [self.hist_args] + ([self.cur_args] if sp.current else []):
+            a.workspace = self.workspace.data_ptr()
+            a.workspace_bytes = self.workspace.numel()
+        # with a single part and no local part the partial already is the
+        # merged latent; the combine is skipped
+        self.skip_combine = (P == 1 and not sp.current and pdt == odt
+                             and self.parts_lse.dtype == torch.float32)
+
+    def run(self, stream=None):
+        if self.absorb:
+            L.mla_q_absorb(self.q_nope, self.w_uk, self.q_lat, stream)
+        L.mla_decode_partial(self.hist_args, stream)
+        if self.w.spec.current:
+            L.mla_decode_partial(self.cur_args, stream)
+        if self.skip_combine:
+            x = self.parts_out[0]
+        else:
+            L.mla_lse_combine(self.parts_out, self.parts_lse, self.lat, self.lse,
+                              local_out=self.cur_out if self.w.spec.current else None,
+                              local_lse=self.cur_lse if self.w.spec.current else None,
+                              stream=stream)
+            x = self.lat
+        L.mla_vup(x, self.w_uv, self.out, stream)
+        return self.out
+
+    def final_lse(self) -> torch.Tensor:
+        return self.parts_lse[0] if self.skip_combine else self.lse
+
+    def final_latent(self) -> torch.Tensor:
+        return self.parts_out[0] if self.skip_combine else self.lat

@@ -1,0 +1,142 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments on the host before any HIP call."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+from mla_split_kv_absorbed_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_decode.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(L.LIB_PATH),
+                                reason="libmla_decode.so not built")
+
+FAKE = 0x10000  # non-NULL, never dereferenced: every case below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(mla_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"mla_decode_partial", "mla_lse_combine", "mla_vup", "mla_q_absorb",
+            "mla_decode_partial_workspace_size", "mla_status_string",
+            "mla_abi_version"} <= set(names)
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}\b", out), n
+
+
+def test_version_and_status_strings():
+    assert L.mla_abi_version() == 1
+    for code, name in L.STATUS.items():
+        assert L.mla_status_string(code).startswith(name)
+    assert L.mla_status_string(12345) == "unknown status"
+
+
+def base_args(**over):
+    a = L.PartialArgs()
+    a.q_lat, a.q_rope, a.kv = FAKE, FAKE + 0x10000000, FAKE + 0x20000000
+    a.q_dtype = a.kv_dtype = L.MLA_BF16
+    a.B, a.S, a.H = 2, 1, 128
+    a.block_size, a.block_table = 32, FAKE + 0x30000000
+    a.max_blocks, a.num_blocks = 4, 8
+    a.P = 2
+    a.range_start, a.range_end = FAKE + 0x40000000, FAKE + 0x40001000
+    a.mask, a.scale = L.MLA_MASK_NONE, 1.0 / math.sqrt(192)
+    a.out, a.out_dtype = FAKE + 0x50000000, L.MLA_BF16
+    a.lse, a.lse_dtype = FAKE + 0x60000000, L.MLA_F32
+    a.workspace, a.workspace_bytes = FAKE + 0x70000000, 1 << 40
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def call(a):
+    return L.lib().mla_decode_partial(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q_lat=None), -1), (dict(kv=None), -1), (dict(out=None), -1),
+    (dict(range_end=None), -1), (dict(block_table=None), -1),
+    (dict(q_dtype=7), -3), (dict(out_dtype=-1), -3), (dict(kv_dtype=L.MLA_F16), -3),
+    (dict(P=0), -2), (dict(B=0), -2), (dict(H=0), -2), (dict(S=0), -2),
+    (dict(S=65), -6), (dict(block_size=-1), -2), (dict(max_blocks=0), -2),
+    (dict(num_blocks=0), -2), (dict(block_size=0), -2),
+    (dict(block_size=0, block_table=None, kv_seq_stride=0), -2),
+    (dict(mask=5), -4), (dict(scale=float("nan")), -4), (dict(num_splits=-1), -4),
+    (dict(flags=0x80), -4),
+    (dict(out=FAKE), -8), (dict(lse=FAKE + 0x20000000 + 64), -8),
+    (dict(workspace=FAKE + 0x50000000), -8),
+])
+def test_partial_validation(over, code):
+    assert call(base_args(**over)) == code
+
+
+def test_workspace_checks():
+    a = base_args()
+    need = L.lib().mla_decode_partial_workspace_size(ctypes.byref(a))
+    assert 0 < need < (1 << 40)
+    assert call(base_args(workspace_bytes=need - 1)) == -5
+    assert call(base_args(workspace=None)) == -5
+    # the plain kernel needs no workspace; invalid arguments have no size
+    assert L.lib().mla_decode_partial_workspace_size(
+        ctypes.byref(base_args(flags=L.MLA_FLAG_FORCE_SIMPLE))) == 0
+    assert L.lib().mla_decode_partial_workspace_size(ctypes.byref(base_args(P=0))) == \
+        ctypes.c_size_t(-1).value
+    # a pure function of the sizes: more splits never need less
+    s1 = L.lib().mla_decode_partial_workspace_size(ctypes.byref(base_args(num_splits=1)))
+    s8 = L.lib().mla_decode_partial_workspace_size(ctypes.byref(base_args(num_splits=8)))
+    assert s8 >= s1
+
+
+def test_combine_vup_absorb_validation():
+    lib = L.lib()
+    c = lib.mla_lse_combine
+    # both local pointers or none
+    assert c(FAKE, FAKE + 4096, 2, 1, 0, FAKE * 8, None, 4, 8, FAKE * 16, 1, None, None) == -1
+    assert c(None, None, 0, 1, 0, None, None, 4, 8, FAKE * 16, 1, None, None) == -2
+    assert c(FAKE, FAKE * 4, 2, 9, 0, None, None, 4, 8, FAKE * 16, 1, None, None) == -3
+    assert c(FAKE, FAKE * 4, 2, 1, 0, None, None, 0, 8, FAKE * 16, 1, None, None) == -2
+    assert c(FAKE, FAKE * 4, 2, 1, 0, None, None, 4, 8, FAKE, 1, None, None) == -8
+    assert c(FAKE, FAKE * 4, 2, 1, 0, None, None, 4, 8, None, 1, None, None) == -1
+    assert lib.mla_vup(None, FAKE, FAKE * 2, 4, 8, 1, None) == -1
+    assert lib.mla_vup(FAKE, FAKE * 64, FAKE * 128, 0, 8, 1, None) == -2
+    assert lib.mla_vup(FAKE, FAKE * 64, FAKE * 128, 4, 8, 3, None) == -3
+    assert lib.mla_vup(FAKE, FAKE * 64, FAKE, 4, 8, 1, None) == -8
+    assert lib.mla_q_absorb(FAKE, None, FAKE * 2, 4, 8, 1, None) == -1
+    assert lib.mla_q_absorb(FAKE, FAKE * 64, FAKE * 128, 4, 0, 1, None) == -2
+    assert lib.mla_q_absorb(FAKE, FAKE * 64, FAKE + 100, 4, 8, 1, None) == -8
+
+
+NO_DEVICE = r"""
+import ctypes, math, sys
+sys.path.insert(0, %r)
+from mla_split_kv_absorbed_amd import _lib as L
+from tests.test_abi_cpu import base_args
+print(L.lib().mla_decode_partial(ctypes.byref(base_args()), None))
+print(L.lib().mla_vup(0x10000, 0x20000000, 0x40000000, 4, 8, 1, None))
+"""
+
+
+def test_valid_call_without_device_reports_hip_error():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    r = subprocess.run([sys.executable, "-c", NO_DEVICE % ROOT], capture_output=True, text=True,
+                       timeout=300, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split() == ["-7", "-7"], r.stdout + r.stderr
