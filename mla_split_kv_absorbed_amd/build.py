@@ -20,7 +20,7 @@ ARCH = "gfx950"
 # form of the matrix instructions lets the allocator place them without
 # scratch spills.
 EXTRA_FLAGS = {
-    "partial_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+
 }
 
 

@@ -206,9 +206,10 @@ int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype,
   Extent ins[2] = {{x, (size_t)T * H * kDc * e}, {w_uv, (size_t)H * kDc * kDv * e}};
   Extent outs[1] = {{out, (size_t)T * H * kDv * e}};
   if (any_overlap(outs, 1, ins, 2)) return MLA_ERR_ALIAS;
-  return launch_vup_simple(x, w_uv, out, T, H, dtype, (hipStream_t)stream) == hipSuccess
-             ? MLA_OK
-             : MLA_ERR_HIP;
+  hipError_t he = dtype == MLA_F32
+                    ? launch_vup_simple(x, w_uv, out, T, H, dtype, (hipStream_t)stream)
+                    : launch_vup_mfma(x, w_uv, out, T, H, dtype, (hipStream_t)stream);
+  return he == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 int mla_q_absorb(const void* q_nope, const void* w_uk, void* q_lat, int T, int H, int dtype,
@@ -220,10 +221,10 @@ int mla_q_absorb(const void* q_nope, const void* w_uk, void* q_lat, int T, int H
   Extent ins[2] = {{q_nope, (size_t)T * H * kDn * e}, {w_uk, (size_t)H * kDc * kDn * e}};
   Extent outs[1] = {{q_lat, (size_t)T * H * kDc * e}};
   if (any_overlap(outs, 1, ins, 2)) return MLA_ERR_ALIAS;
-  return launch_absorb_simple(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream) ==
-                 hipSuccess
-             ? MLA_OK
-             : MLA_ERR_HIP;
+  hipError_t he = dtype == MLA_F32
+                    ? launch_absorb_simple(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream)
+                    : launch_absorb_mfma(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream);
+  return he == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"

@@ -1,0 +1,178 @@
+// Per-head GEMMs of the decode step on CDNA4 matrix cores (bf16 / fp16 in,
+// fp32 accumulate, one rounding to the output type):
+//
+//   q absorption  q_lat^T[c][t] = sum_j W_UK[h][c][j] q_nope[t][h][j]
+//     Both operands are contiguous along the contraction index j, so they
+//     are read straight from global memory into MFMA operand registers.
+//   V-up          out^T[v][t]   = sum_c W_UV[h][c][v] x[t][h][c]
+//     W_UV[h] is stored [c][v] (v contiguous) but the matrix instruction wants
+//     8 consecutive c per lane: the head's 64-column slice is staged in LDS
+//     and read with the transposed LDS read. x is read directly; the result
+//     is written in its batch-major [T][H][128] layout without any transpose
+//     pass (the fused, transpose-free V-up).
+//
+// Computing the transposed products puts 4 consecutive output columns in
+// each lane, so every store is one 8-byte write.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+#define LDS_AS __attribute__((address_space(3)))
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct GT;
+template <> struct GT<bf16> {
+  typedef bf16x8 v8;
+  typedef bf16x4 v4;
+  static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct GT<f16> {
+  typedef f16x8 v8;
+  typedef f16x4 v4;
+  static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// q absorption: grid (H, 2 halves of c, ceil(T/32)), 4 waves, each wave two
+// 32-row c tiles of one 32-token block.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ qn,
+                                                          const T* __restrict__ wuk,
+                                                          T* __restrict__ ql, int Tn, int H) {
+  typedef typename GT<T>::v8 v8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x;
+  const int c0 = blockIdx.y * 256 + wave * 64;
+  const int t0 = blockIdx.z * 32;
+  const int r = lane & 31, hi = lane >> 5;
+  const int t = t0 + r;
+  // B = q_nope^T: column t, 8 consecutive j per k step
+  v8 b[kDn / 16];
+#pragma unroll
+  for (int k = 0; k < kDn / 16; ++k) {
+    if (t < Tn)
+      b[k] = *(const v8*)(qn + ((size_t)t * H + h) * kDn + k * 16 + hi * 8);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[k][i] = (T)0.f;
+  }
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const int c = c0 + ct * 32;
+    const T* wr = wuk + ((size_t)h * kDc + c + r) * kDn + hi * 8;
+    floatx16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kDn / 16; ++k) acc = GT<T>::mfma(*(const v8*)(wr + k * 16), b[k], acc);
+    if (t < Tn) {
+      T* dst = ql + ((size_t)t * H + h) * kDc + c + 4 * hi;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typename GT<T>::v4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (T)acc[4 * g + i];
+        *(typename GT<T>::v4*)(dst + 8 * g) = v;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// V-up: grid (H, 2 halves of v, ceil(T/32)), 2 waves, each wave one 32-column
+// v tile of one 32-token block; W_UV[h][:, 64-column half] staged in LDS.
+// ---------------------------------------------------------------------------
+constexpr int kVupCols = 64;
+constexpr int kVupRow = kVupCols * 2 + 32;  // bytes per LDS row (padded)
+
+template <typename T>
+__global__ __launch_bounds__(128) void vup_mfma_kernel(const T* __restrict__ x,
+                                                       const T* __restrict__ wuv,
+                                                       T* __restrict__ out, int Tn, int H) {
+  typedef typename GT<T>::v8 v8;
+  __shared__ __attribute__((aligned(16))) char ws[kDc * kVupRow];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, vh = blockIdx.y * kVupCols;
+  const int t0 = blockIdx.z * 32;
+  // stage W_UV[h][c][vh : vh+64]: 512 rows x 128 B, 8 x 16 B per row
+  const T* wsrc = wuv + (size_t)h * kDc * kDv + vh;
+  for (int i = tid; i < kDc * 8; i += 128) {
+    const int c = i >> 3, q = i & 7;
+    *(v8*)(ws + c * kVupRow + q * 16) = *(const v8*)(wsrc + (size_t)c * kDv + q * 8);
+  }
+  const int r = lane & 31, hi = lane >> 5;
+  const int t = t0 + r;
+  __syncthreads();
+  // A = W^T (rows v, k = c) by transposed reads: 16-lane block g16 covers
+  // v 16(g16&1)..+15 and c rows 8(g16>>1).. of each 16-wide k step
+  const int j16 = lane & 15, g16 = lane >> 4;
+  const int a_off = ((8 * (g16 >> 1) + (j16 >> 2)) * kVupRow) +
+                    (wave * 32 + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+  floatx16 acc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+  const T* xr = x + ((size_t)t * H + h) * kDc + hi * 8;
+#pragma unroll 8
+  for (int k = 0; k < kDc / 16; ++k) {
+    v8 b;
+    if (t < Tn)
+      b = *(const v8*)(xr + k * 16);
+    else
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = (T)0.f;
+    const char* a0 = ws + a_off + k * 16 * kVupRow;
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)a0);
+    const shortx4 h4 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + 4 * kVupRow));
+    const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
+    acc = GT<T>::mfma(a, b, acc);
+  }
+  if (t < Tn) {
+    T* dst = out + ((size_t)t * H + h) * kDv + vh + wave * 32 + 4 * hi;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      typename GT<T>::v4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (T)acc[4 * g + i];
+      *(typename GT<T>::v4*)(dst + 8 * g) = v;
+    }
+  }
+}
+
+hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int Tn, int H, int dt,
+                              hipStream_t st) {
+  dim3 g(H, kDc / 256, (Tn + 31) / 32);
+  if (dt == MLA_BF16)
+    hipLaunchKernelGGL(absorb_mfma_kernel<bf16>, g, dim3(256), 0, st, (const bf16*)qn,
+                       (const bf16*)w, (bf16*)ql, Tn, H);
+  else
+    hipLaunchKernelGGL(absorb_mfma_kernel<f16>, g, dim3(256), 0, st, (const f16*)qn,
+                       (const f16*)w, (f16*)ql, Tn, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_vup_mfma(const void* x, const void* w, void* out, int Tn, int H, int dt,
+                           hipStream_t st) {
+  dim3 g(H, kDv / kVupCols, (Tn + 31) / 32);
+  if (dt == MLA_BF16)
+    hipLaunchKernelGGL(vup_mfma_kernel<bf16>, g, dim3(128), 0, st, (const bf16*)x,
+                       (const bf16*)w, (bf16*)out, Tn, H);
+  else
+    hipLaunchKernelGGL(vup_mfma_kernel<f16>, g, dim3(128), 0, st, (const f16*)x,
+                       (const f16*)w, (f16*)out, Tn, H);
+  return hipGetLastError();
+}
+
+}  // namespace mla

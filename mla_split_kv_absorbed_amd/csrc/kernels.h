@@ -28,6 +28,10 @@ size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits);
 hipError_t launch_combine(const CombineParams& c, hipStream_t st);
 hipError_t launch_vup_simple(const void* x, const void* w, void* out, int T, int H, int dt,
                              hipStream_t st);
+hipError_t launch_vup_mfma(const void* x, const void* w, void* out, int T, int H, int dt,
+                           hipStream_t st);
+hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int T, int H, int dt,
+                              hipStream_t st);
 hipError_t launch_absorb_simple(const void* qn, const void* w, void* ql, int T, int H, int dt,
                                 hipStream_t st);
 

@@ -13,18 +13,24 @@
 //   LDS --ds_read_b128--> key operand of S^T = K Q^T (32x32x16 MFMA, Q in VGPRs)
 //   online softmax in registers (each lane holds 16 tokens of one head)
 //   LDS --ds_read_b64_tr_b16--> transposed value operand of O^T += C^T P^T
-// LDS layout of a stage is chunk-major: the 16-byte chunk c (8 values) of
-// key row r sits at slot c*32 + (r ^ 4*(c&1)). One LDS-direct load covers
-// two chunk columns for all 32 rows, so every lane's source offset is one
-// register plus a scalar per load; key-operand reads are 512 contiguous bytes
-// per half wave, and the transposed reads of the value operand touch two
-// disjoint 64-byte bank ranges per 16 lanes (the XOR with c&1).
+// LDS layout of a stage is row-major, 1152 bytes per key row, with the 16-byte
+// chunks of row r permuted within each 128-byte group: chunk c sits at
+// position c ^ swz(r). Every LDS-direct load instruction then reads 1 KB of
+// contiguous HBM (whole cache lines) and both operand read patterns are free
+// of bank conflicts (see swz).
 //
 // Each wave owns 32 heads: Q^T for them stays in 144 VGPRs, the fp32 output
-// O^T (512 x 32) in 256 accumulation registers. Softmax uses a lazily updated
-// reference maximum (rescale only when a head's maximum grows by more than
-// 2^8), which keeps every probability <= 256 and the final normalisation
-// exact.
+// O^T (512 x 32) in 256 accumulation registers (AGPRs).
+//
+// Softmax without rescaling the accumulators. Every head's exponent reference
+// m_ref is its first visible score maximum; later weights 2^(x - m_ref) may
+// grow up to 2^64. Floating-point results are invariant under that common
+// scale (the output is divided by the same sum, the LSE adds m_ref back), and
+// 2^64 keeps fp32 accumulations far from overflow. If a later tile exceeds
+// the headroom (adversarial scores), the wave flags it and, after the loop,
+// the workgroup replays the chunk once with each head's exact maximum as the
+// reference. The hot loop therefore never touches the output accumulators
+// outside the matrix instructions.
 //
 // Ranges that need splitting (few sequences, long ranges) are cut into
 // chunks; chunk results go to a fp32 workspace and a second kernel merges
@@ -54,23 +60,63 @@ constexpr int kLoadsWave = kStageBytes / 16 / 64 / kWaves;  // 9
 constexpr int kKSteps = kRow / 16;             // 36
 constexpr int kDTiles = kDc / 32;              // 16
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRescaleThresh = 8.0f;         // log2 units
+constexpr float kHeadroom = 64.0f;             // log2 units: weights stay <= 2^64
+
+// chunk permutation inside a row: position = chunk ^ swz(row). The LDS has
+// 64 four-byte banks; a 16-byte read serves 16 lanes per cycle and the 8-byte
+// transposed read 32 lanes. swz gives the 8 even (and the 8 odd) rows of any
+// 16 consecutive rows distinct positions, so the 16 rows of a key-operand
+// read cover all 64 banks once, and it makes rows 4m and 4m+2 differ in
+// position bit 2, so the 4 rows x 2 chunks of a transposed read do too
+// (both measured conflict-free with the SQ_LDS_BANK_CONFLICT counter).
+__device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
 
 static_assert(kLoadsWave * 64 * 16 * kWaves == kStageBytes, "stage load split");
+static_assert(2 * kLoadsWave < 64, "vmcnt range");
 
 
+// s_waitcnt vmcnt(n) with expcnt / lgkmcnt unconstrained (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14)
+#define MLA_VMCNT(n) (((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+
+// Wait until the LDS-direct loads of the current tile have landed. Per tile a
+// wave issues kLoadsWave loads; n_after = number of tiles issued after the
+// current one (loads complete in issue order).
 __device__ __forceinline__ void wait_vm(int n_after) {
-  // vmcnt(9 * n_after); expcnt / lgkmcnt left unconstrained
-  if (n_after >= 2) __builtin_amdgcn_s_waitcnt(0x4F72);       // vmcnt(18)
-  else if (n_after == 1) __builtin_amdgcn_s_waitcnt(0x0F79);  // vmcnt(9)
-  else __builtin_amdgcn_s_waitcnt(0x0F70);                    // vmcnt(0)
+  if (n_after >= 2) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(2 * kLoadsWave));
+  else if (n_after == 1) __builtin_amdgcn_s_waitcnt(MLA_VMCNT(kLoadsWave));
+  else __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0));
 }
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(MLA_VMCNT(0)); }
 
+// The key-score product S^T = K Q^T is issued as inline assembly with its
+// accumulator pinned to VGPRs, so that the 256 fp32 output accumulators of
+// the value product (compiler-issued, AGPR form) and the 144 registers of
+// Q^T fit the register file together. The compiler does not model the
+// latency of these instructions: reading the scores with vector ALU
+// instructions is preceded by qk_drain(), which covers the result latency
+// of the last ones and carries the accumulators as operands.
 template <typename T> struct MT;
 template <> struct MT<bf16> {
   typedef bf16x8 v8;
   static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ void qk_first(floatx16& acc, v8 a, v8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void qk_next(floatx16& acc, v8 a, v8 b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  }
+  // starts two chains in one statement: the early-clobber outputs cannot
+  // alias any operand of either instruction
+  static __device__ __forceinline__ void qk_first2(floatx16& acc, floatx16& acc2, v8 a, v8 b,
+                                                   v8 a2, v8 b2) {
+    asm volatile(
+        "v_mfma_f32_32x32x16_bf16 %0, %2, %3, 0\n\t"
+        "v_mfma_f32_32x32x16_bf16 %1, %4, %5, 0"
+        : "=&v"(acc), "=&v"(acc2)
+        : "v"(a), "v"(b), "v"(a2), "v"(b2));
   }
 };
 template <> struct MT<f16> {
@@ -78,7 +124,30 @@ template <> struct MT<f16> {
   static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  static __device__ __forceinline__ void qk_first(floatx16& acc, v8 a, v8 b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void qk_next(floatx16& acc, v8 a, v8 b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+  }
+  // starts two chains in one statement: the early-clobber outputs cannot
+  // alias any operand of either instruction
+  static __device__ __forceinline__ void qk_first2(floatx16& acc, floatx16& acc2, v8 a, v8 b,
+                                                   v8 a2, v8 b2) {
+    asm volatile(
+        "v_mfma_f32_32x32x16_f16 %0, %2, %3, 0\n\t"
+        "v_mfma_f32_32x32x16_f16 %1, %4, %5, 0"
+        : "=&v"(acc), "=&v"(acc2)
+        : "v"(a), "v"(b), "v"(a2), "v"(b2));
+  }
 };
+
+// Wait states after the last score products before any other instruction
+// reads their results (more than the 8-pass result latency rule requires).
+// The accumulators are in/out operands, so no reader can be scheduled above.
+__device__ __forceinline__ void qk_drain(floatx16& a, floatx16& b) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
+}
 
 // ---------------------------------------------------------------------------
 // the plan: tiles, chunks and split slots of one call, computed in-kernel
@@ -137,7 +206,7 @@ struct Found {
   int u, tb, te, slot, nsplit, split_idx;
 };
 
-__device__ Plan make_plan(const PartialParams& pp, int want, Found* found, int* sh) {
+__device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Found* found, int* sh) {
   const int tid = threadIdx.x;
   const int U = pp.P * pp.B;
   const int per = (U + 255) / 256;
@@ -227,21 +296,45 @@ struct MfmaParams {
   intx4* ws_desc;
 };
 
+// One LDS-direct load: 64 lanes x 16 bytes from the buffer `rs` at
+// voffset + soffset into LDS [m0, m0 + 1024) (lane i lands at m0 + 16 i).
+// Issued as assembly so that the compiler adds no waits of its own for these
+// loads; the tile pipeline waits for them explicitly (wait_vm + barrier).
+// M0 is written here and nothing else in the kernel uses it.
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned m0, int voffset,
+                                           int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rs), "s"(soffset)
+               : "memory");
+}
+
+// Normalised output of one head row: lane (head, hi) holds latent values
+// 32 d + 8 g + 4 hi + 0..3 in o[d][4 g + 0..3]; one 4-element vector store each.
+template <typename TO>
+__device__ __forceinline__ void store_rows(TO* dst, const floatx16* o, int hi, float inv,
+                                           bool bad) {
+  typedef TO v4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int d = 0; d < kDTiles; ++d)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      v4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = from_f<TO>(bad ? NAN : o[d][4 * g + i] * inv);
+      *(v4*)(dst + d * 32 + 8 * g + 4 * hi) = v;
+    }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
   typedef typename MT<T>::v8 v8;
-  // one LDS object per stage, so the compiler can tell a stage's reads from
-  // the loads still landing in the other stages
-  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
-  auto stage_ptr = [&](int st) -> char* {
-    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
-  };
+  // the LDS ring: kStages stages of one 32-token tile each
+  __shared__ __attribute__((aligned(1024))) char lds[kStages * kStageBytes];
   __shared__ int sh_scan[256];
   __shared__ Found sh_found;
+  __shared__ int sh_redo;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -259,7 +352,10 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     chunk = grp * 8 + (r & 7);
     s = r >> 3;
   }
-  if (tid == 0) sh_found.u = -1;
+  if (tid == 0) {
+    sh_found.u = -1;
+    sh_redo = 0;
+  }
   __syncthreads();
   const Plan pl = make_plan(pp, chunk, &sh_found, sh_scan);
   __syncthreads();
@@ -289,13 +385,36 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const int hi = lane >> 5;          // 0/1: which half of a 16-wide k step
   const int r32 = lane & 31;         // key row (QK) / head column
   const int head = wave * kHeadsWave + r32;
-  // key operand: row r32, chunk 2k + hi  -> k*1024 + qk_lane
-  const int qk_lane = hi * 512 + ((r32 ^ (4 * hi)) << 4);
-  // value operand (transposed read): chunk 4d + 2(g16&1) + x, row 16kk + 8e + 4h + q
-  const int j16 = lane & 15, g16 = lane >> 4, q4 = j16 >> 2, xx = (j16 & 3) >> 1;
-  const int pv_lane = (2 * (g16 & 1) + xx) * 512 + ((4 * (hi ^ xx) + q4) << 4) + ((j16 & 1) << 3);
-  // LDS-direct loads: load g covers chunks 2g, 2g+1; lane -> (row, chunk parity)
-  const int ld_lane = ((r32 ^ (4 * hi)) * kRowBytes) + hi * 16;
+  // key operand of k step k: row r32, chunk 2k + hi, at
+  // qk_off[k & 3] + (k >> 2) * 128
+  int qk_off[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) qk_off[m] = r32 * kRowBytes + (((2 * m + hi) ^ swz(r32)) << 4);
+  // value operand (transposed read) of latent tile d, token half kk: 16-lane
+  // group g16 reads rows 16kk + 8f + 4hi + q4 (f = 0, 1: the two reads) and
+  // chunk 4d + 2(g16&1) + (j16&3)/2, at pv_off[d & 1][f] + (d >> 1) * 128 +
+  // 16 kk * 1152
+  const int j16 = lane & 15, g16 = lane >> 4, q4 = j16 >> 2;
+  int pv_off[2][2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const int row = 8 * f + 4 * hi + q4;
+      const int lo = (4 * e + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz(row);
+      pv_off[e][f] = row * kRowBytes + (lo << 4) + ((j16 & 1) << 3);
+    }
+  // LDS-direct loads: load i of this wave fills slots (9 wave + i) * 64 + lane,
+  // slot = row * 72 + position; the source is that row's chunk position ^ swz(row)
+  int ld_off[kLoadsWave];
+#pragma unroll
+  for (int i = 0; i < kLoadsWave; ++i) {
+    const int slot = (wave * kLoadsWave + i) * 64 + lane;
+    const int r = slot / kChunksRow, pos = slot % kChunksRow;
+    ld_off[i] = r * kRowBytes + ((pos ^ swz(r)) << 4);
+  }
+  const unsigned lds_base =
+      __builtin_amdgcn_readfirstlane((unsigned)(size_t)(LDS_AS char*)lds);
 
   // ---- Q^T for this wave's 32 heads, in registers -------------------------
   v8 q[kKSteps];
@@ -308,76 +427,115 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       q[k] = d < kDc ? *(const v8*)(ql + d) : *(const v8*)(qr + (d - kDc));
     }
   }
+  // Complete the Q loads here: with nothing pending at loop entry the
+  // compiler places no vmcnt waits of its own inside the tile loop (it cannot
+  // see the LDS-direct loads, and a wait for an early Q load would otherwise
+  // drain every tile in flight).
+  wait_vm_all();
 
   floatx16 o[kDTiles];
 #pragma unroll
   for (int i = 0; i < kDTiles; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[i][j] = 0.f;
-  float m_ref = -INFINITY, l_part = 0.f, l_round = 0.f;
+  float m_ref = -INFINITY, m_seen = -INFINITY, l_part = 0.f, l_round = 0.f;
+  bool over = false;    // a score exceeded m_ref + headroom
+  bool compute = true;  // false: this wave only keeps the shared loads going
   bool bad = unit_bad;
   const float sl2 = pp.scale * kLog2e;
 
   const int tb = fd.tb, te = unit_bad ? fd.tb : fd.te;
   const int st_tile = st / kTile;
   const char* kvb = (const char*)pp.kv;
+  // scalars used inside the tile lambdas (keeps the argument block out of
+  // private memory)
+  const int block_size = pp.block_size, max_blocks = pp.max_blocks;
+  const int num_blocks = pp.num_blocks, kv_seq_stride = pp.kv_seq_stride;
+  const __attribute__((address_space(4))) int* btab =
+      (const __attribute__((address_space(4))) int*)pp.block_table;
 
-  // tile -> (first token, token count, buffer resource)
-  auto tile_tok0 = [&](int j) { return j == 0 ? st : (st_tile + j) * kTile; };
-  auto issue = [&](int j, int stage) {
-    const int tok0 = tile_tok0(j);
-    const int tok1 = min(en, (st_tile + j + 1) * kTile);
-    const char* base;
-    int nrows = tok1 - tok0;
-    if (pp.block_size > 0) {
-      const int id = ((const __attribute__((address_space(4))) int*)
-                          pp.block_table)[(size_t)b * pp.max_blocks + tok0 / pp.block_size];
-      if (id < 0 || id >= pp.num_blocks) {
-        bad = true;
-        nrows = 0;
-        base = kvb;
+  // tile j of the range: first token, and the LDS-direct loads of its rows
+  auto tile_tok0 = [&](int j) __attribute__((always_inline)) {
+    return j == 0 ? st : (st_tile + j) * kTile;
+  };
+  // buffer resource over the rows of tile j (zero rows past the range or for a
+  // bad block id: those loads return zeros without touching memory)
+  auto tile_rsrc = [&](int j, bool& is_bad) __attribute__((always_inline)) {
+    const char* base = kvb;
+    int nrows = 0;
+    if (j < te) {
+      const int tok0 = tile_tok0(j);
+      nrows = min(en, (st_tile + j + 1) * kTile) - tok0;
+      if (block_size > 0) {
+        const int id = btab[(size_t)b * max_blocks + tok0 / block_size];
+        if (id < 0 || id >= num_blocks) {
+          is_bad = true;
+          nrows = 0;
+        } else {
+          base = kvb + ((size_t)id * block_size + (tok0 % block_size)) * kRowBytes;
+        }
       } else {
-        base = kvb + ((size_t)id * pp.block_size + (tok0 % pp.block_size)) * kRowBytes;
+        base = kvb + ((size_t)b * kv_seq_stride + tok0) * kRowBytes;
       }
-    } else {
-      base = kvb + ((size_t)b * pp.kv_seq_stride + tok0) * kRowBytes;
     }
-    __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrows * kRowBytes, 0x00020000);
-    char* dst = stage_ptr(stage) + wave * kLoadsWave * 1024;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrows * kRowBytes,
+                                             0x00020000);
+  };
+  // LDS-direct loads of tile j into `stage`
+  auto issue = [&](int j, int stage) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(j, bad);
+    const unsigned m0 = lds_base + stage * kStageBytes + wave * kLoadsWave * 1024;
 #pragma unroll
-    for (int i = 0; i < kLoadsWave; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + i * 1024), 16, ld_lane,
-                                               (wave * kLoadsWave + i) * 32, 0, 0);
+    for (int i = 0; i < kLoadsWave; ++i) lds_load16(rs, m0 + i * 1024, ld_off[i], 0);
   };
 
-  // ---- prologue: 3 tiles in flight -----------------------------------------
-#pragma unroll
-  for (int i = 0; i < kStages - 1; ++i)
-    if (tb + i < te) issue(tb + i, i);
-
-  auto step = [&](int j, int stage) {
+  auto step = [&](int j, int stage, bool replay) __attribute__((always_inline)) {
     wait_vm(min(2, te - 1 - j));
     __syncthreads();
-    if (j + kStages - 1 < te) issue(j + kStages - 1, (stage + kStages - 1) % kStages);
-    const char* sb = stage_ptr(stage);
+    if (j + kStages - 1 < te) issue(j + kStages - 1, (stage + kStages - 1) & (kStages - 1));
+    if (!compute) return;
+    const char* sb = lds + stage * kStageBytes;
 
-    // S^T = K . Q^T over 576 dims; key operands prefetched 4 k-steps ahead,
-    // scheduling fences keep the prefetch window (and register use) bounded
-    floatx16 sacc;
+    // S^T = K . Q^T over 576 dims as two independent accumulation chains
+    // (k steps 0..17 and 18..35, issued alternately: a dependent matrix
+    // instruction would wait for its predecessor's result). Key operands
+    // rotate through a 5-entry ring, loaded 3 instructions ahead: a register
+    // is refilled only after the instruction two slots back has issued, so an
+    // LDS return can never overwrite an operand of a queued instruction (the
+    // compiler does not track these assembly instructions' operands).
+    constexpr int kHalf = kKSteps / 2;
+    constexpr int kRing = 5, kAhead = 3;
+    auto kstep = [](int n) { return (n & 1) ? kHalf + (n >> 1) : (n >> 1); };
+    auto kaddr = [&](int k) __attribute__((always_inline)) {
+      return (const v8*)(sb + qk_off[k & 3] + (k >> 2) * 128);
+    };
+    floatx16 sacc, sacc2;
+    v8 kb[kRing];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    v8 kb[4];
+    for (int n = 0; n < kAhead; ++n) kb[n] = *kaddr(kstep(n));
 #pragma unroll
-    for (int k = 0; k < 4; ++k) kb[k] = *(const v8*)(sb + qk_lane + k * 1024);
-#pragma unroll
-    for (int k = 0; k < kKSteps; ++k) {
-      sacc = MT<T>::mfma(kb[k & 3], q[k], sacc);
-      if (k + 4 < kKSteps)
-        kb[k & 3] = *(const v8*)(sb + qk_lane + (k + 4) * 1024);
+    for (int n = 0; n < kKSteps; ++n) {
+      const int k = kstep(n);
+      if (n == 0) {
+        // both chains start together (n = 0 and n = 1)
+        kb[kAhead % kRing] = *kaddr(kstep(kAhead));
+        MT<T>::qk_first2(sacc, sacc2, kb[0], q[0], kb[1], q[kHalf]);
+        kb[(kAhead + 1) % kRing] = *kaddr(kstep(kAhead + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        continue;
+      }
+      if (n == 1) continue;
+      if (n & 1)
+        MT<T>::qk_next(sacc2, kb[n % kRing], q[k]);
+      else
+        MT<T>::qk_next(sacc, kb[n % kRing], q[k]);
+      if (n + kAhead < kKSteps) kb[(n + kAhead) % kRing] = *kaddr(kstep(n + kAhead));
       __builtin_amdgcn_sched_barrier(0);
     }
-    // mask, scale (log2 domain), running maximum
+    qk_drain(sacc, sacc2);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] += sacc2[i];
+    // mask, scale (log2 domain), tile maximum of each head
     const int tok0 = tile_tok0(j);
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
     float mloc = -INFINITY;
@@ -388,19 +546,10 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       mloc = fmaxf(mloc, sacc[i]);
     }
     const float mt = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const bool need = mt > m_ref + kRescaleThresh;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float mn = need ? mt : m_ref;
-      const float alpha = need ? (m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - mn))
-                               : 1.f;
-      l_part *= alpha;
-      l_round *= alpha;
-#pragma unroll
-      for (int d = 0; d < kDTiles; ++d) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[d][i] *= alpha;
-      }
-      m_ref = mn;
+    if (!replay) {
+      m_seen = fmaxf(m_seen, mt);
+      if (m_ref == -INFINITY) m_ref = mt;  // first visible scores set the reference
+      over |= mt > m_ref + kHeadroom;
     }
     v8 pb[2];
 #pragma unroll
@@ -417,29 +566,57 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
 
     // O^T += C^T . P^T, C = the tile's 512 latent columns; transposed value
     // operands prefetched 2 MFMAs ahead
-    auto vload = [&](int n) {
+    auto vload = [&](int n) __attribute__((always_inline)) {
       const int d = n >> 1, kk = n & 1;
-      const char* a0 = sb + pv_lane + d * 2048 + kk * 256;
-      const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)a0);
-      const shortx4 h4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + 128));
+      const char* a0 = sb + (d >> 1) * 128 + 16 * kk * kRowBytes;
+      const shortx4 lo =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[d & 1][0]));
+      const shortx4 h4 =
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[d & 1][1]));
       return __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
+    // token half kk outer, latent tile d inner: consecutive instructions
+    // accumulate into different tiles
     v8 vb[3];
     vb[0] = vload(0);
-    vb[1] = vload(1);
+    vb[1] = vload(2);
 #pragma unroll
     for (int n = 0; n < 2 * kDTiles; ++n) {
-      if (n + 2 < 2 * kDTiles) vb[(n + 2) % 3] = vload(n + 2);
-      o[n >> 1] = MT<T>::mfma(vb[n % 3], pb[n & 1], o[n >> 1]);
+      const int m = ((n & (kDTiles - 1)) << 1) | (n / kDTiles);  // (d, kk) -> d*2 + kk
+      if (n + 2 < 2 * kDTiles) {
+        const int m2 = (((n + 2) & (kDTiles - 1)) << 1) | ((n + 2) / kDTiles);
+        vb[(n + 2) % 3] = vload(m2);
+      }
+      o[m >> 1] = MT<T>::mfma(vb[n % 3], pb[m & 1], o[m >> 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  for (int j = tb; j < te; j += kStages) {
-    step(j, 0);
-    if (j + 1 < te) step(j + 1, 1);
-    if (j + 2 < te) step(j + 2, 2);
-    if (j + 3 < te) step(j + 3, 3);
+  auto run_tiles = [&](bool replay) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kStages - 1; ++i)
+      if (tb + i < te) issue(tb + i, i);
+#pragma clang loop unroll(disable)
+    for (int j = tb; j < te; ++j) step(j, (j - tb) & (kStages - 1), replay);
+  };
+  run_tiles(false);
+
+  // replay the chunk if any wave ran out of exponent headroom
+  if (__builtin_amdgcn_ballot_w64(over) && lane == 0) atomicOr(&sh_redo, 1 << wave);
+  __syncthreads();
+  const int redo = __builtin_amdgcn_readfirstlane(sh_redo);
+  if (redo) {
+    compute = (redo >> wave) & 1;
+    if (compute) {
+      m_ref = m_seen;
+      l_part = l_round = 0.f;
+#pragma unroll
+      for (int d = 0; d < kDTiles; ++d)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
+    }
+    __syncthreads();
+    run_tiles(true);
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -459,15 +636,13 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const size_t row = fd.slot < 0 ? ((size_t)p * Tq + t) * pp.H + head
                                  : ((size_t)fd.slot * S + s) * pp.H + head;
   if (fd.slot < 0) {
-#pragma unroll
-    for (int d = 0; d < kDTiles; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const size_t col = (size_t)d * 32 + 8 * g + 4 * hi;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          store_any(pp.out, row * kDc + col + i, pp.out_dtype, bad ? NAN : o[d][4 * g + i] * inv);
-      }
+    // each lane holds 4 consecutive latent values per (tile, group)
+    if (pp.out_dtype == MLA_F32)
+      store_rows<float>((float*)pp.out + row * kDc, o, hi, inv, bad);
+    else if (pp.out_dtype == MLA_BF16)
+      store_rows<bf16>((bf16*)pp.out + row * kDc, o, hi, inv, bad);
+    else
+      store_rows<f16>((f16*)pp.out + row * kDc, o, hi, inv, bad);
     if (hi == 0) store_any(pp.lse, row, pp.lse_dtype, lse);
   } else {
     float* dst = pp.ws_out + row * kDc;
