@@ -61,6 +61,7 @@ constexpr int kKSteps = kRow / 16;             // 36
 constexpr int kDTiles = kDc / 32;              // 16
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kHeadroom = 64.0f;             // log2 units: weights stay <= 2^64
+constexpr int kIdCache = 256;                  // block ids staged in LDS per refill
 
 // chunk permutation inside a row: position = chunk ^ swz(row). The LDS has
 // 64 four-byte banks; a 16-byte read serves 16 lanes per cycle and the 8-byte
@@ -335,6 +336,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   __shared__ int sh_scan[256];
   __shared__ Found sh_found;
   __shared__ int sh_redo;
+  __shared__ int sh_ids[kIdCache];  // first cache row of tiles [id_base, id_base + 256)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -451,60 +453,94 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   // private memory)
   const int block_size = pp.block_size, max_blocks = pp.max_blocks;
   const int num_blocks = pp.num_blocks, kv_seq_stride = pp.kv_seq_stride;
-  const __attribute__((address_space(4))) int* btab =
-      (const __attribute__((address_space(4))) int*)pp.block_table;
 
   // tile j of the range: first token, and the LDS-direct loads of its rows
   auto tile_tok0 = [&](int j) __attribute__((always_inline)) {
     return j == 0 ? st : (st_tile + j) * kTile;
   };
-  // buffer resource over the rows of tile j (zero rows past the range or for a
-  // bad block id: those loads return zeros without touching memory)
-  auto tile_rsrc = [&](int j, bool& is_bad) __attribute__((always_inline)) {
+  // The first cache row (block id * block size + slot, or the contiguous row)
+  // of each of the chunk's tiles is staged in LDS by vector code, kIdCache
+  // tiles per refill, so the tile loop does no division and no scalar loads
+  // (whose out-of-order return would stall every LDS wait behind them).
+  // -1 marks a tile past the range or a bad block id.
+  int id_base = tb;
+  auto fill_rows = [&](int from) __attribute__((always_inline)) {
+    __syncthreads();
+    for (int i = tid; i < kIdCache; i += 256) {
+      const int j = from + i;
+      int row = -1;
+      if (j < te) {
+        const int tok0 = tile_tok0(j);
+        if (block_size > 0) {
+          const int id = pp.block_table[(size_t)b * max_blocks + tok0 / block_size];
+          if (id >= 0 && id < num_blocks) row = id * block_size + tok0 % block_size;
+        } else {
+          row = b * kv_seq_stride + tok0;
+        }
+      }
+      sh_ids[i] = row;
+    }
+    wait_vm_all();
+    __syncthreads();
+  };
+  int seg_end = te;  // end of the current segment (pipeline bound)
+  auto tile_row = [&](int j) __attribute__((always_inline)) -> int {
+    if (j >= seg_end) return -1;
+    return __builtin_amdgcn_readfirstlane(sh_ids[j - id_base]);
+  };
+  // buffer resource over the rows of tile j starting at cache row `row`
+  // (zero rows past the range or for a bad block id: those loads return zeros
+  // without touching memory)
+  auto tile_rsrc = [&](int j, int row) __attribute__((always_inline)) {
     const char* base = kvb;
     int nrows = 0;
     if (j < te) {
-      const int tok0 = tile_tok0(j);
-      nrows = min(en, (st_tile + j + 1) * kTile) - tok0;
-      if (block_size > 0) {
-        const int id = btab[(size_t)b * max_blocks + tok0 / block_size];
-        if (id < 0 || id >= num_blocks) {
-          is_bad = true;
-          nrows = 0;
-        } else {
-          base = kvb + ((size_t)id * block_size + (tok0 % block_size)) * kRowBytes;
-        }
+      if (row < 0) {
+        bad = true;
       } else {
-        base = kvb + ((size_t)b * kv_seq_stride + tok0) * kRowBytes;
+        base = kvb + (size_t)(unsigned)row * kRowBytes;
+        nrows = min(en, (st_tile + j + 1) * kTile) - tile_tok0(j);
       }
     }
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nrows * kRowBytes,
                                              0x00020000);
   };
-  // LDS-direct loads of tile j into `stage`
-  auto issue = [&](int j, int stage) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(j, bad);
+  // LDS-direct loads of tile j into `stage` (prologue)
+  auto issue = [&](int j, int stage, int id) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t rs = tile_rsrc(j, id);
     const unsigned m0 = lds_base + stage * kStageBytes + wave * kLoadsWave * 1024;
 #pragma unroll
     for (int i = 0; i < kLoadsWave; ++i) lds_load16(rs, m0 + i * 1024, ld_off[i], 0);
   };
+  // the first row of the next tile to issue is read one step ahead
+  int next_id = -1;
 
   auto step = [&](int j, int stage, bool replay) __attribute__((always_inline)) {
-    wait_vm(min(2, te - 1 - j));
+    wait_vm(min(2, seg_end - 1 - j));
     __syncthreads();
-    if (j + kStages - 1 < te) issue(j + kStages - 1, (stage + kStages - 1) & (kStages - 1));
+    // the loads of tile j + 3 go into the stage every wave finished reading
+    // before this barrier; they are spread over the score product below so
+    // the CU's address unit drains them while the matrix unit works
+    const bool do_issue = j + kStages - 1 < seg_end;
+    __amdgpu_buffer_rsrc_t nrs = tile_rsrc(do_issue ? j + kStages - 1 : te, next_id);
+    const unsigned nm0 =
+        lds_base + ((stage + kStages - 1) & (kStages - 1)) * kStageBytes + wave * kLoadsWave * 1024;
+    if (do_issue) next_id = tile_row(j + kStages);
+    auto issue_part = [&](int i) __attribute__((always_inline)) {
+      if (do_issue) lds_load16(nrs, nm0 + i * 1024, ld_off[i], 0);
+    };
     if (!compute) return;
     const char* sb = lds + stage * kStageBytes;
 
     // S^T = K . Q^T over 576 dims as two independent accumulation chains
     // (k steps 0..17 and 18..35, issued alternately: a dependent matrix
     // instruction would wait for its predecessor's result). Key operands
-    // rotate through a 5-entry ring, loaded 3 instructions ahead: a register
+    // rotate through a 6-entry ring, loaded 4 instructions ahead: a register
     // is refilled only after the instruction two slots back has issued, so an
     // LDS return can never overwrite an operand of a queued instruction (the
     // compiler does not track these assembly instructions' operands).
     constexpr int kHalf = kKSteps / 2;
-    constexpr int kRing = 5, kAhead = 3;
+    constexpr int kRing = 6, kAhead = 4;
     auto kstep = [](int n) { return (n & 1) ? kHalf + (n >> 1) : (n >> 1); };
     auto kaddr = [&](int k) __attribute__((always_inline)) {
       return (const v8*)(sb + qk_off[k & 3] + (k >> 2) * 128);
@@ -530,21 +566,27 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       else
         MT<T>::qk_next(sacc, kb[n % kRing], q[k]);
       if (n + kAhead < kKSteps) kb[(n + kAhead) % kRing] = *kaddr(kstep(n + kAhead));
+      if ((n & 3) == 2) issue_part(n >> 2);  // n = 2, 6, ..., 34: loads 0..8
       __builtin_amdgcn_sched_barrier(0);
     }
     qk_drain(sacc, sacc2);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] += sacc2[i];
-    // mask, scale (log2 domain), tile maximum of each head
+    // mask, tile maximum of each head (scores in log2 units are sacc * sl2;
+    // sl2 > 0, so the maximum is taken on the raw sums)
     const int tok0 = tile_tok0(j);
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
     float mloc = -INFINITY;
+    if (nvis < kTile) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 8 * (i >> 2) + 4 * hi + (i & 3);
-      sacc[i] = row < nvis ? sacc[i] * sl2 : -INFINITY;
-      mloc = fmaxf(mloc, sacc[i]);
+      for (int i = 0; i < 16; ++i) {
+        const int row = 8 * (i >> 2) + 4 * hi + (i & 3);
+        sacc[i] = row < nvis ? sacc[i] : -INFINITY;
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
+    mloc *= sl2;
     const float mt = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     if (!replay) {
       m_seen = fmaxf(m_seen, mt);
@@ -556,7 +598,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     for (int i = 0; i < 16; ++i) {
       // the output is normalised by the same rounded weights the matrix
       // product uses; the LSE comes from the unrounded ones
-      const float pf = sacc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sacc[i] - m_ref);
+      const float pf =
+          sacc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -m_ref));
       const T pt = (T)pf;
       l_part += pf;
       l_round += (float)pt;
@@ -565,7 +608,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     __builtin_amdgcn_sched_barrier(0);
 
     // O^T += C^T . P^T, C = the tile's 512 latent columns; transposed value
-    // operands prefetched 2 MFMAs ahead
+    // operands prefetched 3 instructions ahead
     auto vload = [&](int n) __attribute__((always_inline)) {
       const int d = n >> 1, kk = n & 1;
       const char* a0 = sb + (d >> 1) * 128 + 16 * kk * kRowBytes;
@@ -577,27 +620,35 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     };
     // token half kk outer, latent tile d inner: consecutive instructions
     // accumulate into different tiles
-    v8 vb[3];
-    vb[0] = vload(0);
-    vb[1] = vload(2);
+    constexpr int kVRing = 5, kVAhead = 3;
+    auto vm = [](int n) { return ((n & (kDTiles - 1)) << 1) | (n / kDTiles); };  // -> d*2 + kk
+    v8 vb[kVRing];
+#pragma unroll
+    for (int n = 0; n < kVAhead; ++n) vb[n] = vload(vm(n));
 #pragma unroll
     for (int n = 0; n < 2 * kDTiles; ++n) {
-      const int m = ((n & (kDTiles - 1)) << 1) | (n / kDTiles);  // (d, kk) -> d*2 + kk
-      if (n + 2 < 2 * kDTiles) {
-        const int m2 = (((n + 2) & (kDTiles - 1)) << 1) | ((n + 2) / kDTiles);
-        vb[(n + 2) % 3] = vload(m2);
-      }
-      o[m >> 1] = MT<T>::mfma(vb[n % 3], pb[m & 1], o[m >> 1]);
+      const int m = vm(n);
+      if (n + kVAhead < 2 * kDTiles) vb[(n + kVAhead) % kVRing] = vload(vm(n + kVAhead));
+      o[m >> 1] = MT<T>::mfma(vb[n % kVRing], pb[m & 1], o[m >> 1]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // Tiles run in segments of up to kIdCache: the row table is refilled and
+  // the load pipeline restarted between segments (outside the tile loop).
   auto run_tiles = [&](bool replay) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < kStages - 1; ++i)
-      if (tb + i < te) issue(tb + i, i);
 #pragma clang loop unroll(disable)
-    for (int j = tb; j < te; ++j) step(j, (j - tb) & (kStages - 1), replay);
+    for (int seg = tb; seg < te; seg += kIdCache) {
+      id_base = seg;
+      seg_end = min(te, seg + kIdCache);
+      fill_rows(seg);
+#pragma unroll
+      for (int i = 0; i < kStages - 1; ++i)
+        if (seg + i < seg_end) issue(seg + i, i, tile_row(seg + i));
+      next_id = tile_row(seg + kStages - 1);
+#pragma clang loop unroll(disable)
+      for (int j = seg; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1), replay);
+    }
   };
   run_tiles(false);
 
