@@ -95,6 +95,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain device copy of 512 MiB three times (the "
+                         "calibration kernel for the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -109,6 +112,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        n = 256 * 1024 * 1024
+        x = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 2 * n, "copy_probe_bytes_written": 2 * n,
+                          "launches": 3}), flush=True)
+        return
     L.lib()  # fail loudly if the HIP library is missing
     sp = W.SPECS[args.workload]
     print(f"[bench] generating workload {sp.name}", file=sys.stderr, flush=True)
