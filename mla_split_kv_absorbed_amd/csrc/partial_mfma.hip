@@ -19,24 +19,30 @@
 // contiguous HBM (whole cache lines) and both operand read patterns are free
 // of bank conflicts (see swz).
 //
-// Each wave owns 32 heads: Q^T for them stays in 144 VGPRs, the fp32 output
-// O^T (512 x 32) in 256 accumulation registers (AGPRs).
+// Each wave owns 32 heads for the score product: Q^T for them stays in 144
+// VGPRs. The softmax weights of all heads then go through an 8 KB LDS buffer
+// and each wave runs the value product for all 128 heads over its own 128
+// latent columns, so every transposed value operand feeds 4 matrix
+// instructions; the fp32 output O^T (128 x 128 per wave) stays in 256
+// accumulation registers (AGPRs).
 //
-// Softmax without rescaling the accumulators. Every head's exponent reference
-// m_ref is its first visible score maximum; later weights 2^(x - m_ref) may
-// grow up to 2^64. Floating-point results are invariant under that common
-// scale (the output is divided by the same sum, the LSE adds m_ref back), and
-// 2^64 keeps fp32 accumulations far from overflow. If a later tile exceeds
-// the headroom (adversarial scores), the wave flags it and, after the loop,
-// the workgroup replays the chunk once with each head's exact maximum as the
-// reference. The hot loop therefore never touches the output accumulators
-// outside the matrix instructions.
+// Softmax without rescaling the accumulators. The first pass uses the fixed
+// exponent reference 0: weights are 2^(score in log2 units). Floating-point
+// results are invariant under a common scale (the output is divided by the
+// same sum, the LSE adds the reference back), so this is exact as long as
+// every head's maximum lies in [-64, 64] (no overflow, no underflow of the
+// dominant weights). A chunk where some head leaves that window (adversarial
+// scores) is replayed once with each head's exact maximum as the reference.
+// The hot loop therefore never touches the output accumulators outside the
+// matrix instructions and needs no cross-lane maximum per tile.
 //
 // Ranges that need splitting (few sequences, long ranges) are cut into
 // chunks; chunk results go to a fp32 workspace and a second kernel merges
 // them by LSE in a fixed order.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace mla {
 
@@ -48,11 +54,14 @@ typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef int intx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;                      // 4 x 32 heads = 128 heads per group
 constexpr int kHeadsWave = 32;
 constexpr int kHeadsGroup = kWaves * kHeadsWave;
 constexpr int kStages = 4;
+constexpr int kAheadTiles = kStages - 1;       // tiles in flight while one is computed
 constexpr int kRowBytes = kRow * 2;            // 1152
 constexpr int kChunksRow = kRowBytes / 16;     // 72
 constexpr int kStageBytes = kTile * kRowBytes; // 36864
@@ -60,7 +69,8 @@ constexpr int kLoadsWave = kStageBytes / 16 / 64 / kWaves;  // 9
 constexpr int kKSteps = kRow / 16;             // 36
 constexpr int kDTiles = kDc / 32;              // 16
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kHeadroom = 64.0f;             // log2 units: weights stay <= 2^64
+constexpr float kHeadroom = 64.0f;  // log2 units: first-pass weights stay <= 2^64
+constexpr float kFloor = 64.0f;     // ... and the largest one >= 2^-64
 constexpr int kIdCache = 256;                  // block ids staged in LDS per refill
 
 // chunk permutation inside a row: position = chunk ^ swz(row). The LDS has
@@ -71,6 +81,13 @@ constexpr int kIdCache = 256;                  // block ids staged in LDS per re
 // position bit 2, so the 4 rows x 2 chunks of a transposed read do too
 // (both measured conflict-free with the SQ_LDS_BANK_CONFLICT counter).
 __device__ __forceinline__ int swz(int r) { return (((r >> 1) & 1) << 2) | ((r >> 2) & 3); }
+
+// Weight buffer: one 64-byte row of 32 tokens per head; chunk c (tokens
+// 8c .. 8c + 7) of head h sits at position c ^ ((h >> 2) & 3). The 16 lanes
+// of a 16-byte read (16 consecutive heads, one chunk) then cover all 64
+// banks.
+constexpr int kPRow = kTile * 2;  // 64 bytes
+__device__ __forceinline__ int pchunk(int c, int h) { return c ^ ((h >> 2) & 3); }
 
 static_assert(kLoadsWave * 64 * 16 * kWaves == kStageBytes, "stage load split");
 static_assert(2 * kLoadsWave < 64, "vmcnt range");
@@ -106,6 +123,10 @@ template <> struct MT<bf16> {
   static __device__ __forceinline__ void qk_first(floatx16& acc, v8 a, v8 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
   }
+  // c + a.x + a.y in one dot instruction
+  static __device__ __forceinline__ float sum2(bf16x2 a, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, (bf16x2){(bf16)1.f, (bf16)1.f}, c, false);
+  }
   static __device__ __forceinline__ void qk_next(floatx16& acc, v8 a, v8 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
   }
@@ -127,6 +148,9 @@ template <> struct MT<f16> {
   }
   static __device__ __forceinline__ void qk_first(floatx16& acc, v8 a, v8 b) {
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ float sum2(f16x2 a, float c) {
+    return __builtin_amdgcn_fdot2(a, (f16x2){(f16)1.f, (f16)1.f}, c, false);
   }
   static __device__ __forceinline__ void qk_next(floatx16& acc, v8 a, v8 b) {
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
@@ -310,20 +334,21 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned m
                : "memory");
 }
 
-// Normalised output of one head row: lane (head, hi) holds latent values
-// 32 d + 8 g + 4 hi + 0..3 in o[d][4 g + 0..3]; one 4-element vector store each.
+// Normalised output of head 32 g + (lane & 31) over this wave's 128 latent
+// columns: lane (head, hi) holds columns 32 dt + 8 j + 4 hi + 0..3 in
+// o[4 dt + g][4 j + 0..3]; one 4-element vector store each.
 template <typename TO>
-__device__ __forceinline__ void store_rows(TO* dst, const floatx16* o, int hi, float inv,
+__device__ __forceinline__ void store_rows(TO* dst, const floatx16* o, int g, int hi, float inv,
                                            bool bad) {
   typedef TO v4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-  for (int d = 0; d < kDTiles; ++d)
+  for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    for (int j = 0; j < 4; ++j) {
       v4 v;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = from_f<TO>(bad ? NAN : o[d][4 * g + i] * inv);
-      *(v4*)(dst + d * 32 + 8 * g + 4 * hi) = v;
+      for (int i = 0; i < 4; ++i) v[i] = from_f<TO>(bad ? NAN : o[4 * dt + g][4 * j + i] * inv);
+      *(v4*)(dst + dt * 32 + 8 * j + 4 * hi) = v;
     }
 }
 
@@ -337,6 +362,10 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   __shared__ Found sh_found;
   __shared__ int sh_redo;
   __shared__ int sh_ids[kIdCache];  // first cache row of tiles [id_base, id_base + 256)
+  // softmax weights of the current tile, all heads: [head][32 tokens] bf16 /
+  // fp16, 16-byte chunks permuted by pchunk
+  __shared__ __attribute__((aligned(16))) char sh_p[kHeadsGroup * kPRow];
+  __shared__ float sh_inv[kHeadsGroup];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -392,20 +421,29 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   int qk_off[4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) qk_off[m] = r32 * kRowBytes + (((2 * m + hi) ^ swz(r32)) << 4);
-  // value operand (transposed read) of latent tile d, token half kk: 16-lane
-  // group g16 reads rows 16kk + 8f + 4hi + q4 (f = 0, 1: the two reads) and
-  // chunk 4d + 2(g16&1) + (j16&3)/2, at pv_off[d & 1][f] + (d >> 1) * 128 +
-  // 16 kk * 1152
+  // value operand (transposed read) of latent tile dt (this wave's columns
+  // 128 wave + 32 dt ..) and token half kk: 16-lane group g16 reads rows
+  // 16 kk + 8 hi + 4 f + q4 (f = 0, 1: the two reads, k = 8 hi + 4 f + e is
+  // token 16 kk + k) and chunk 16 wave + 4 dt + 2 (g16 & 1) + (j16 & 3) / 2,
+  // at pv_off[dt & 1][f] + (dt >> 1) * 128 + 16 kk * 1152
   const int j16 = lane & 15, g16 = lane >> 4, q4 = j16 >> 2;
   int pv_off[2][2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
-      const int row = 8 * f + 4 * hi + q4;
-      const int lo = (4 * e + 2 * (g16 & 1) + ((j16 & 3) >> 1)) ^ swz(row);
-      pv_off[e][f] = row * kRowBytes + (lo << 4) + ((j16 & 1) << 3);
+      const int row = 8 * hi + 4 * f + q4;
+      const int c = 16 * wave + 4 * e + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+      pv_off[e][f] = row * kRowBytes + ((c ^ swz(row)) << 4) + ((j16 & 1) << 3);
     }
+  // weight operand P^T of head group g, token half kk: head 32 g + r32,
+  // tokens 16 kk + 8 hi .. + 7, at pw_off[kk] + g * 32 * kPRow
+  int pw_off[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) pw_off[kk] = r32 * kPRow + (pchunk(2 * kk + hi, r32) << 4);
+  // this wave's softmax weights of head `head`, tokens 8 j + 4 hi .. + 3, go
+  // to pst_off + (pchunk(j, r32) << 4)
+  const int pst_off = head * kPRow + 8 * hi;
   // LDS-direct loads: load i of this wave fills slots (9 wave + i) * 64 + lane,
   // slot = row * 72 + position; the source is that row's chunk position ^ swz(row)
   int ld_off[kLoadsWave];
@@ -440,9 +478,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   for (int i = 0; i < kDTiles; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[i][j] = 0.f;
-  float m_ref = -INFINITY, m_seen = -INFINITY, l_part = 0.f, l_round = 0.f;
-  bool over = false;    // a score exceeded m_ref + headroom
-  bool compute = true;  // false: this wave only keeps the shared loads going
+  // exponent reference (log2 units): 0 on the first pass, the head's exact
+  // maximum on a replay
+  float m_ref = 0.f, m_seen = -INFINITY, l_part = 0.f, l_round = 0.f;
   bool bad = unit_bad;
   const float sl2 = pp.scale * kLog2e;
 
@@ -512,24 +550,30 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
 #pragma unroll
     for (int i = 0; i < kLoadsWave; ++i) lds_load16(rs, m0 + i * 1024, ld_off[i], 0);
   };
-  // the first row of the next tile to issue is read one step ahead
+  // the first row of the next tile to issue is known one step ahead; the
+  // row after it is read from LDS one more step ahead (pend_row), so the
+  // read's latency never stalls a step
   int next_id = -1;
+  int pend_row = -1;
 
-  auto step = [&](int j, int stage, bool replay) __attribute__((always_inline)) {
-    wait_vm(min(2, seg_end - 1 - j));
+  auto step = [&](int j, int stage) __attribute__((always_inline)) {
+    wait_vm(min(kAheadTiles - 1, seg_end - 1 - j));
     __syncthreads();
-    // the loads of tile j + 3 go into the stage every wave finished reading
+    // the loads of tile j + kAheadTiles go into the stage every wave finished reading
     // before this barrier; they are spread over the score product below so
     // the CU's address unit drains them while the matrix unit works
-    const bool do_issue = j + kStages - 1 < seg_end;
-    __amdgpu_buffer_rsrc_t nrs = tile_rsrc(do_issue ? j + kStages - 1 : te, next_id);
+    const bool do_issue = j + kAheadTiles < seg_end;
+    __amdgpu_buffer_rsrc_t nrs = tile_rsrc(do_issue ? j + kAheadTiles : te, next_id);
     const unsigned nm0 =
-        lds_base + ((stage + kStages - 1) & (kStages - 1)) * kStageBytes + wave * kLoadsWave * 1024;
-    if (do_issue) next_id = tile_row(j + kStages);
+        lds_base + ((stage + kAheadTiles) & (kStages - 1)) * kStageBytes + wave * kLoadsWave * 1024;
+    if (do_issue) {
+      next_id = __builtin_amdgcn_readfirstlane(pend_row);
+      const int jn = j + kAheadTiles + 2;
+      pend_row = jn < seg_end ? sh_ids[jn - id_base] : -1;
+    }
     auto issue_part = [&](int i) __attribute__((always_inline)) {
       if (do_issue) lds_load16(nrs, nm0 + i * 1024, ld_off[i], 0);
     };
-    if (!compute) return;
     const char* sb = lds + stage * kStageBytes;
 
     // S^T = K . Q^T over 576 dims as two independent accumulation chains
@@ -572,11 +616,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     qk_drain(sacc, sacc2);
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] += sacc2[i];
-    // mask, tile maximum of each head (scores in log2 units are sacc * sl2;
-    // sl2 > 0, so the maximum is taken on the raw sums)
+    // mask (only a range's last tile can be partial; exp2(-inf) = 0)
     const int tok0 = tile_tok0(j);
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
-    float mloc = -INFINITY;
     if (nvis < kTile) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
@@ -584,90 +626,99 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
         sacc[i] = row < nvis ? sacc[i] : -INFINITY;
       }
     }
+    // this lane's running maximum of the raw sums (checked after the pass;
+    // scores in log2 units are sacc * sl2 with sl2 > 0)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[i]);
-    mloc *= sl2;
-    const float mt = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    if (!replay) {
-      m_seen = fmaxf(m_seen, mt);
-      if (m_ref == -INFINITY) m_ref = mt;  // first visible scores set the reference
-      over |= mt > m_ref + kHeadroom;
-    }
-    v8 pb[2];
+    for (int i = 0; i < 16; ++i) m_seen = fmaxf(m_seen, sacc[i]);
+    // weights 2^(sacc * sl2 - m_ref) to the shared buffer: lane (head, hi)
+    // holds tokens 8 j + 4 hi + 0..3 in sacc[4 j + 0..3]. The output is
+    // normalised by the sum of the rounded weights the matrix product uses,
+    // the LSE comes from the unrounded ones.
+    typedef T t2 __attribute__((ext_vector_type(2)));
+    typedef T t4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      // the output is normalised by the same rounded weights the matrix
-      // product uses; the LSE comes from the unrounded ones
-      const float pf =
-          sacc[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(fmaf(sacc[i], sl2, -m_ref));
-      const T pt = (T)pf;
-      l_part += pf;
-      l_round += (float)pt;
-      pb[i >> 3][i & 7] = pt;
+    for (int j4 = 0; j4 < 4; ++j4) {
+      float pf[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pf[e] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * j4 + e], sl2, -m_ref));
+        l_part += pf[e];
+      }
+      const t2 lo = {(T)pf[0], (T)pf[1]}, hi2 = {(T)pf[2], (T)pf[3]};
+      l_round = MT<T>::sum2(lo, l_round);
+      l_round = MT<T>::sum2(hi2, l_round);
+      *(t4*)(sh_p + pst_off + (pchunk(j4, r32) << 4)) = __builtin_shufflevector(lo, hi2, 0, 1, 2, 3);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // every wave's weights are in sh_p
 
-    // O^T += C^T . P^T, C = the tile's 512 latent columns; transposed value
-    // operands prefetched 3 instructions ahead
-    auto vload = [&](int n) __attribute__((always_inline)) {
-      const int d = n >> 1, kk = n & 1;
-      const char* a0 = sb + (d >> 1) * 128 + 16 * kk * kRowBytes;
+    // O^T += C^T . P^T for this wave's 128 latent columns and all 128 heads:
+    // per token half, 4 value operands (transposed reads of the tile) times
+    // 4 weight operands; each value operand feeds 4 consecutive instructions
+    // into different accumulators
+    auto vload = [&](int dt, int kk) __attribute__((always_inline)) {
+      const char* a0 = sb + (dt >> 1) * 128 + 16 * kk * kRowBytes;
       const shortx4 lo =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[d & 1][0]));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[dt & 1][0]));
       const shortx4 h4 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[d & 1][1]));
+          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[dt & 1][1]));
       return __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
     };
-    // token half kk outer, latent tile d inner: consecutive instructions
-    // accumulate into different tiles
-    constexpr int kVRing = 5, kVAhead = 3;
-    auto vm = [](int n) { return ((n & (kDTiles - 1)) << 1) | (n / kDTiles); };  // -> d*2 + kk
-    v8 vb[kVRing];
+    auto wload = [&](int g, int kk) __attribute__((always_inline)) {
+      return *(const v8*)(sh_p + pw_off[kk] + g * kHeadsWave * kPRow);
+    };
+    v8 wb[2][kWaves];
+    v8 va[3];
 #pragma unroll
-    for (int n = 0; n < kVAhead; ++n) vb[n] = vload(vm(n));
+    for (int g = 0; g < kWaves; ++g) wb[0][g] = wload(g, 0);
+    va[0] = vload(0, 0);
+    va[1] = vload(1, 0);
 #pragma unroll
-    for (int n = 0; n < 2 * kDTiles; ++n) {
-      const int m = vm(n);
-      if (n + kVAhead < 2 * kDTiles) vb[(n + kVAhead) % kVRing] = vload(vm(n + kVAhead));
-      o[m >> 1] = MT<T>::mfma(vb[n % kVRing], pb[m & 1], o[m >> 1]);
+    for (int n = 0; n < 8; ++n) {
+      const int dt = n & 3, kk = n >> 2;
+      if (n + 2 < 8) va[(n + 2) % 3] = vload((n + 2) & 3, (n + 2) >> 2);
+      if (n == 1)
+#pragma unroll
+        for (int g = 0; g < kWaves; ++g) wb[1][g] = wload(g, 1);
+#pragma unroll
+      for (int g = 0; g < kWaves; ++g) o[dt * 4 + g] = MT<T>::mfma(va[n % 3], wb[kk][g], o[dt * 4 + g]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   // Tiles run in segments of up to kIdCache: the row table is refilled and
   // the load pipeline restarted between segments (outside the tile loop).
-  auto run_tiles = [&](bool replay) __attribute__((always_inline)) {
+  auto run_tiles = [&]() __attribute__((always_inline)) {
 #pragma clang loop unroll(disable)
     for (int seg = tb; seg < te; seg += kIdCache) {
       id_base = seg;
       seg_end = min(te, seg + kIdCache);
       fill_rows(seg);
 #pragma unroll
-      for (int i = 0; i < kStages - 1; ++i)
+      for (int i = 0; i < kAheadTiles; ++i)
         if (seg + i < seg_end) issue(seg + i, i, tile_row(seg + i));
-      next_id = tile_row(seg + kStages - 1);
+      next_id = tile_row(seg + kAheadTiles);
+      pend_row = tile_row(seg + kAheadTiles + 1);
 #pragma clang loop unroll(disable)
-      for (int j = seg; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1), replay);
+      for (int j = seg; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1));
     }
   };
-  run_tiles(false);
+  run_tiles();
 
-  // replay the chunk if any wave ran out of exponent headroom
+  // replay the chunk with exact maxima if any head's maximum left the window
+  const float m_head = fmaxf(m_seen, __shfl_xor(m_seen, 32, 64)) * sl2;
+  const bool over = m_head > kHeadroom || (m_head < -kFloor && m_head != -INFINITY);
   if (__builtin_amdgcn_ballot_w64(over) && lane == 0) atomicOr(&sh_redo, 1 << wave);
   __syncthreads();
   const int redo = __builtin_amdgcn_readfirstlane(sh_redo);
   if (redo) {
-    compute = (redo >> wave) & 1;
-    if (compute) {
-      m_ref = m_seen;
-      l_part = l_round = 0.f;
+    m_ref = m_head == -INFINITY ? 0.f : m_head;
+    l_part = l_round = 0.f;
 #pragma unroll
-      for (int d = 0; d < kDTiles; ++d)
+    for (int d = 0; d < kDTiles; ++d)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
-    }
+      for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
     __syncthreads();
-    run_tiles(true);
+    run_tiles();
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -684,32 +735,29 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     inv = 0.f;
     lse = -INFINITY;
   }
-  const size_t row = fd.slot < 0 ? ((size_t)p * Tq + t) * pp.H + head
-                                 : ((size_t)fd.slot * S + s) * pp.H + head;
-  if (fd.slot < 0) {
-    // each lane holds 4 consecutive latent values per (tile, group)
-    if (pp.out_dtype == MLA_F32)
-      store_rows<float>((float*)pp.out + row * kDc, o, hi, inv, bad);
-    else if (pp.out_dtype == MLA_BF16)
-      store_rows<bf16>((bf16*)pp.out + row * kDc, o, hi, inv, bad);
+  // the normaliser of each head comes from the wave that ran its softmax
+  if (hi == 0) sh_inv[head] = inv;
+  const size_t row0 = fd.slot < 0 ? ((size_t)p * Tq + t) * pp.H : ((size_t)fd.slot * S + s) * pp.H;
+  if (hi == 0) {
+    if (fd.slot < 0)
+      store_any(pp.lse, row0 + head, pp.lse_dtype, lse);
     else
-      store_rows<f16>((f16*)pp.out + row * kDc, o, hi, inv, bad);
-    if (hi == 0) store_any(pp.lse, row, pp.lse_dtype, lse);
-  } else {
-    float* dst = pp.ws_out + row * kDc;
+      pp.ws_lse[row0 + head] = lse;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int d = 0; d < kDTiles; ++d)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = d * 32 + 8 * g + 4 * hi;
-        float4 v;
-        v.x = bad ? NAN : o[d][4 * g + 0] * inv;
-        v.y = bad ? NAN : o[d][4 * g + 1] * inv;
-        v.z = bad ? NAN : o[d][4 * g + 2] * inv;
-        v.w = bad ? NAN : o[d][4 * g + 3] * inv;
-        *(float4*)(dst + col) = v;
-      }
-    if (hi == 0) pp.ws_lse[row] = lse;
+  for (int g = 0; g < kWaves; ++g) {
+    const int h = g * kHeadsWave + r32;
+    const float ig = sh_inv[h];
+    const size_t e0 = (row0 + h) * kDc + kDc / kWaves * wave;
+    if (fd.slot >= 0)
+      store_rows<float>(pp.ws_out + e0, o, g, hi, ig, bad);
+    else if (pp.out_dtype == MLA_F32)
+      store_rows<float>((float*)pp.out + e0, o, g, hi, ig, bad);
+    else if (pp.out_dtype == MLA_BF16)
+      store_rows<bf16>((bf16*)pp.out + e0, o, g, hi, ig, bad);
+    else
+      store_rows<f16>((f16*)pp.out + e0, o, g, hi, ig, bad);
   }
 }
 
@@ -717,45 +765,73 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
 // merge of split chunks (fixed order), one wave per (unit, query, head) row
 // ---------------------------------------------------------------------------
 
+template <typename TO>
+__device__ __forceinline__ void store8(TO* dst, const float* v) {
+  typedef TO v8o __attribute__((ext_vector_type(8)));
+  v8o x;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = from_f<TO>(v[i]);
+  *(v8o*)dst = x;
+}
+
+// Lane i holds the LSE of chunk i0 + i; the chunks' partial rows are then
+// accumulated in ascending order, 4 rows in flight.
 __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
   const int lane = threadIdx.x & 63;
   const int n_units = *mp.ws_count;
   const long long rows = (long long)n_units * pp.S * pp.H;
   const int Tq = pp.B * pp.S;
-  for (long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
-       r += (long long)gridDim.x * 4) {
+  const long long waves = (long long)gridDim.x * 4;
+  for (long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows; r += waves) {
     const int h = (int)(r % pp.H);
     const int s = (int)((r / pp.H) % pp.S);
     const int k = (int)(r / ((long long)pp.H * pp.S));
     const intx4 dsc = mp.ws_desc[k];
     const int u = dsc[0], slot0 = dsc[1], n = dsc[2];
+    auto wrow = [&](int i) { return ((size_t)(slot0 + i) * pp.S + s) * pp.H + h; };
     float m = -INFINITY;
     bool nan_seen = false;
-    for (int i = 0; i < n; ++i) {
-      const float li = pp.ws_lse[((size_t)(slot0 + i) * pp.S + s) * pp.H + h];
+    for (int i0 = 0; i0 < n; i0 += 64) {
+      const float li = i0 + lane < n ? pp.ws_lse[wrow(i0 + lane)] : -INFINITY;
       nan_seen |= isnan(li);
       m = fmaxf(m, li);
     }
+    m = wave_max(m);
+    nan_seen = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float z = 0.f;
     if (m != -INFINITY && !nan_seen) {
-      for (int i = 0; i < n; ++i) {
-        const size_t wr = ((size_t)(slot0 + i) * pp.S + s) * pp.H + h;
-        const float li = pp.ws_lse[wr];
-        if (li == -INFINITY) continue;
-        const float w = expf(li - m);
-        z += w;
-        const float4* src = (const float4*)(pp.ws_out + wr * kDc + lane * 8);
-        const float4 a = src[0], c = src[1];
-        acc[0] = fmaf(w, a.x, acc[0]);
-        acc[1] = fmaf(w, a.y, acc[1]);
-        acc[2] = fmaf(w, a.z, acc[2]);
-        acc[3] = fmaf(w, a.w, acc[3]);
-        acc[4] = fmaf(w, c.x, acc[4]);
-        acc[5] = fmaf(w, c.y, acc[5]);
-        acc[6] = fmaf(w, c.z, acc[6]);
-        acc[7] = fmaf(w, c.w, acc[7]);
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        const int cnt = min(64, n - i0);
+        const float li = lane < cnt ? pp.ws_lse[wrow(i0 + lane)] : -INFINITY;
+        const float wl = li == -INFINITY ? 0.f : expf(li - m);
+        z += wave_sum(wl);
+        for (int i = 0; i < cnt; i += 4) {
+          float4 a[4], c[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (i + q < cnt) {
+              const float4* src = (const float4*)(pp.ws_out + wrow(i0 + i + q) * kDc + lane * 8);
+              a[q] = src[0];
+              c[q] = src[1];
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float w = __shfl(wl, i + q, 64);
+            if (i + q < cnt && w != 0.f) {
+              acc[0] = fmaf(w, a[q].x, acc[0]);
+              acc[1] = fmaf(w, a[q].y, acc[1]);
+              acc[2] = fmaf(w, a[q].z, acc[2]);
+              acc[3] = fmaf(w, a[q].w, acc[3]);
+              acc[4] = fmaf(w, c[q].x, acc[4]);
+              acc[5] = fmaf(w, c[q].y, acc[5]);
+              acc[6] = fmaf(w, c[q].z, acc[6]);
+              acc[7] = fmaf(w, c[q].w, acc[7]);
+            }
+          }
+        }
       }
     }
     const int p = u / pp.B, b = u % pp.B;
@@ -772,7 +848,13 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
       lse = -INFINITY;
     }
-    for (int i = 0; i < 8; ++i) store_any(pp.out, orow * kDc + lane * 8 + i, pp.out_dtype, acc[i]);
+    const size_t e0 = orow * kDc + lane * 8;
+    if (pp.out_dtype == MLA_F32)
+      store8<float>((float*)pp.out + e0, acc);
+    else if (pp.out_dtype == MLA_BF16)
+      store8<bf16>((bf16*)pp.out + e0, acc);
+    else
+      store8<f16>((f16*)pp.out + e0, acc);
     if (lane == 0) store_any(pp.lse, orow, pp.lse_dtype, lse);
   }
 }
@@ -817,7 +899,15 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
     hipLaunchKernelGGL(partial_mfma_kernel<f16>, grid, dim3(256), 0, st, mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(split_merge_kernel, dim3(kTargetGroups), dim3(256), 0, st, mp);
+  // one wave per merged row: at most min(U, groups) split units (a split
+  // unit has more tiles than a chunk), capped; the kernel strides beyond
+  const size_t split_units = pp_in.num_splits > 1
+                                 ? (size_t)pp_in.P * pp_in.B
+                                 : std::min((size_t)pp_in.P * pp_in.B, (size_t)kTargetGroups);
+  const size_t merge_rows = split_units * pp_in.S * pp_in.H;
+  const unsigned merge_blocks = (unsigned)std::max<size_t>(
+      1, std::min<size_t>((merge_rows + 3) / 4, 2048));
+  hipLaunchKernelGGL(split_merge_kernel, dim3(merge_blocks), dim3(256), 0, st, mp);
   return hipGetLastError();
 }
 
