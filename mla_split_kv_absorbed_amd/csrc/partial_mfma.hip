@@ -43,6 +43,7 @@
 #include "kernels.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace mla {
 
@@ -61,7 +62,8 @@ constexpr int kWaves = 4;                      // 4 x 32 heads = 128 heads per g
 constexpr int kHeadsWave = 32;
 constexpr int kHeadsGroup = kWaves * kHeadsWave;
 constexpr int kStages = 4;
-constexpr int kAheadTiles = kStages - 1;       // tiles in flight while one is computed
+constexpr int kAheadTiles = kStages - 2;       // tiles in flight (one stage computes, one
+                                               // holds the previous tile for its value product)
 constexpr int kRowBytes = kRow * 2;            // 1152
 constexpr int kChunksRow = kRowBytes / 16;     // 72
 constexpr int kStageBytes = kTile * kRowBytes; // 36864
@@ -556,12 +558,96 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   int next_id = -1;
   int pend_row = -1;
 
-  auto step = [&](int j, int stage) __attribute__((always_inline)) {
+  typedef T t2 __attribute__((ext_vector_type(2)));
+  typedef T t4 __attribute__((ext_vector_type(4)));
+
+  // O^T += C^T . P^T for this wave's 128 latent columns and all 128 heads,
+  // C from the stage at `pb`, P^T from sh_p: per token half, 4 value
+  // operands (transposed reads) times 4 weight operands, each value operand
+  // feeding 4 instructions into different accumulators. With `soft`, the
+  // softmax weights of the next tile (raw sums `sacc`) are computed in
+  // between, so their vector work runs in the shadow of the matrix
+  // instructions; they are returned packed in `pk`.
+  // operands of the value product: C^T (transposed reads of the stage at
+  // `pb`) and P^T (from sh_p)
+  auto vload = [&](const char* pb, int dt, int kk) __attribute__((always_inline)) {
+    const char* a0 = pb + (dt >> 1) * 128 + 16 * kk * kRowBytes;
+    const shortx4 lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[dt & 1][0]));
+    const shortx4 h4 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[dt & 1][1]));
+    return __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto wload = [&](int g, int kk) __attribute__((always_inline)) {
+    return *(const v8*)(sh_p + pw_off[kk] + g * kHeadsWave * kPRow);
+  };
+
+  // O^T += C^T . P^T for this wave's 128 latent columns and all 128 heads,
+  // C from the stage at `pb`, P^T from sh_p: per token half, 4 value
+  // operands (transposed reads) times 4 weight operands, each value operand
+  // feeding 4 instructions into different accumulators. The first operands
+  // (weights of token half 0, value operands 0 and 1) arrive in `wb0` /
+  // `va01`, loaded during the preceding score product. With `soft`, the
+  // softmax weights of the next tile (raw scores `sa`) are computed in
+  // between, so their vector work runs in the shadow of the
+  // matrix instructions; they are returned packed in `pk`.
+  auto pv = [&](const char* pb, auto soft, const floatx16& sa, t2* pk, const v8* wb0,
+                const v8* va01) __attribute__((always_inline)) {
+    constexpr bool kSoft = decltype(soft)::value;
+    // weight of score i: 2^(s * sl2 - m_ref) with s = sa[i]; pairs
+    // are packed to the matrix input type. The output is normalised by the
+    // sum of the rounded weights the matrix product uses, the LSE comes from
+    // the unrounded ones. The running maximum of the raw scores is checked
+    // after the pass.
+    float pf_even = 0.f;
+    auto weight = [&](int i) __attribute__((always_inline)) {
+      const float sc = sa[i];
+      m_seen = fmaxf(m_seen, sc);
+      const float pf = __builtin_amdgcn_exp2f(fmaf(sc, sl2, -m_ref));
+      l_part += pf;
+      if (i & 1) {
+        pk[i >> 1] = t2{(T)pf_even, (T)pf};
+        l_round = MT<T>::sum2(pk[i >> 1], l_round);
+      } else {
+        pf_even = pf;
+      }
+    };
+    v8 wb[2][kWaves];
+    v8 va[3];
+#pragma unroll
+    for (int g = 0; g < kWaves; ++g) wb[0][g] = wb0[g];
+    va[0] = va01[0];
+    va[1] = va01[1];
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int dt = n & 3, kk = n >> 2;
+      if (n + 2 < 8) va[(n + 2) % 3] = vload(pb, (n + 2) & 3, (n + 2) >> 2);
+      if (n == 1)
+#pragma unroll
+        for (int g = 0; g < kWaves; ++g) wb[1][g] = wload(g, 1);
+#pragma unroll
+      for (int g = 0; g < kWaves; ++g) {
+        o[dt * 4 + g] = MT<T>::mfma(va[n % 3], wb[kk][g], o[dt * 4 + g]);
+        // one score's weight after every second matrix instruction
+        if constexpr (kSoft) {
+          if ((g & 1) == 0) weight(2 * n + (g >> 1));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if constexpr (!kSoft) __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // One step of the tile pipeline: tile j's score product, then the value
+  // product of tile j - 1 (if `has_prev`) with tile j's softmax in between,
+  // then tile j's weights go to sh_p once every wave is done reading it.
+  auto step = [&](int j, int stage, bool has_prev) __attribute__((always_inline)) {
     wait_vm(min(kAheadTiles - 1, seg_end - 1 - j));
     __syncthreads();
-    // the loads of tile j + kAheadTiles go into the stage every wave finished reading
-    // before this barrier; they are spread over the score product below so
-    // the CU's address unit drains them while the matrix unit works
+    // the loads of tile j + kAheadTiles go into the stage of tile j - 2,
+    // which every wave finished reading before this barrier; they are
+    // spread over the score product so the CU's address unit drains them
+    // while the matrix unit works
     const bool do_issue = j + kAheadTiles < seg_end;
     __amdgpu_buffer_rsrc_t nrs = tile_rsrc(do_issue ? j + kAheadTiles : te, next_id);
     const unsigned nm0 =
@@ -571,9 +657,15 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       const int jn = j + kAheadTiles + 2;
       pend_row = jn < seg_end ? sh_ids[jn - id_base] : -1;
     }
+    // issued on every step: past the segment the resource has no records,
+    // so the loads touch no memory and only zero the stage of tile j - 2
+    // (consumed); every step therefore adds the same count to vmcnt
     auto issue_part = [&](int i) __attribute__((always_inline)) {
-      if (do_issue) lds_load16(nrs, nm0 + i * 1024, ld_off[i], 0);
+      lds_load16(nrs, nm0 + i * 1024, ld_off[i], 0);
     };
+    // the previous tile's stage, for the value product after the scores
+    const char* pb = lds + ((stage + kStages - 1) & (kStages - 1)) * kStageBytes;
+    v8 wb0[kWaves], va01[2];
     const char* sb = lds + stage * kStageBytes;
 
     // S^T = K . Q^T over 576 dims as two independent accumulation chains
@@ -611,6 +703,13 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
         MT<T>::qk_next(sacc, kb[n % kRing], q[k]);
       if (n + kAhead < kKSteps) kb[(n + kAhead) % kRing] = *kaddr(kstep(n + kAhead));
       if ((n & 3) == 2) issue_part(n >> 2);  // n = 2, 6, ..., 34: loads 0..8
+      // first operands of the value product, once the key ring stops loading
+      // (harmless reads of stale data when there is no previous tile)
+      if (n == kKSteps - kAhead + 1)
+#pragma unroll
+        for (int g = 0; g < kWaves; ++g) wb0[g] = wload(g, 0);
+      if (n == kKSteps - kAhead + 2) va01[0] = vload(pb, 0, 0);
+      if (n == kKSteps - kAhead + 3) va01[1] = vload(pb, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
     qk_drain(sacc, sacc2);
@@ -626,63 +725,33 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
         sacc[i] = row < nvis ? sacc[i] : -INFINITY;
       }
     }
-    // this lane's running maximum of the raw sums (checked after the pass;
-    // scores in log2 units are sacc * sl2 with sl2 > 0)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) m_seen = fmaxf(m_seen, sacc[i]);
-    // weights 2^(sacc * sl2 - m_ref) to the shared buffer: lane (head, hi)
-    // holds tokens 8 j + 4 hi + 0..3 in sacc[4 j + 0..3]. The output is
-    // normalised by the sum of the rounded weights the matrix product uses,
-    // the LSE comes from the unrounded ones.
-    typedef T t2 __attribute__((ext_vector_type(2)));
-    typedef T t4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4) {
-      float pf[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pf[e] = __builtin_amdgcn_exp2f(fmaf(sacc[4 * j4 + e], sl2, -m_ref));
-        l_part += pf[e];
-      }
-      const t2 lo = {(T)pf[0], (T)pf[1]}, hi2 = {(T)pf[2], (T)pf[3]};
-      l_round = MT<T>::sum2(lo, l_round);
-      l_round = MT<T>::sum2(hi2, l_round);
-      *(t4*)(sh_p + pst_off + (pchunk(j4, r32) << 4)) = __builtin_shufflevector(lo, hi2, 0, 1, 2, 3);
-    }
-    __syncthreads();  // every wave's weights are in sh_p
+    __builtin_amdgcn_sched_barrier(0);
 
-    // O^T += C^T . P^T for this wave's 128 latent columns and all 128 heads:
-    // per token half, 4 value operands (transposed reads of the tile) times
-    // 4 weight operands; each value operand feeds 4 consecutive instructions
-    // into different accumulators
-    auto vload = [&](int dt, int kk) __attribute__((always_inline)) {
-      const char* a0 = sb + (dt >> 1) * 128 + 16 * kk * kRowBytes;
-      const shortx4 lo =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[dt & 1][0]));
-      const shortx4 h4 =
-          __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + pv_off[dt & 1][1]));
-      return __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    auto wload = [&](int g, int kk) __attribute__((always_inline)) {
-      return *(const v8*)(sh_p + pw_off[kk] + g * kHeadsWave * kPRow);
-    };
-    v8 wb[2][kWaves];
-    v8 va[3];
+    t2 pk[8];
+    if (has_prev) {
+      pv(pb, std::integral_constant<bool, true>(), sacc, pk, wb0, va01);
+    } else {
+      // first tile of a segment: the weights alone (same arithmetic)
+      float pf_even = 0.f;
 #pragma unroll
-    for (int g = 0; g < kWaves; ++g) wb[0][g] = wload(g, 0);
-    va[0] = vload(0, 0);
-    va[1] = vload(1, 0);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      const int dt = n & 3, kk = n >> 2;
-      if (n + 2 < 8) va[(n + 2) % 3] = vload((n + 2) & 3, (n + 2) >> 2);
-      if (n == 1)
-#pragma unroll
-        for (int g = 0; g < kWaves; ++g) wb[1][g] = wload(g, 1);
-#pragma unroll
-      for (int g = 0; g < kWaves; ++g) o[dt * 4 + g] = MT<T>::mfma(va[n % 3], wb[kk][g], o[dt * 4 + g]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < 16; ++i) {
+        const float sc = sacc[i];
+        m_seen = fmaxf(m_seen, sc);
+        const float pf = __builtin_amdgcn_exp2f(fmaf(sc, sl2, -m_ref));
+        l_part += pf;
+        if (i & 1) {
+          pk[i >> 1] = t2{(T)pf_even, (T)pf};
+          l_round = MT<T>::sum2(pk[i >> 1], l_round);
+        } else {
+          pf_even = pf;
+        }
+      }
     }
+    __syncthreads();  // every wave is done reading the previous weights
+#pragma unroll
+    for (int j4 = 0; j4 < 4; ++j4)
+      *(t4*)(sh_p + pst_off + (pchunk(j4, r32) << 4)) =
+          __builtin_shufflevector(pk[2 * j4], pk[2 * j4 + 1], 0, 1, 2, 3);
   };
 
   // Tiles run in segments of up to kIdCache: the row table is refilled and
@@ -698,9 +767,23 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
         if (seg + i < seg_end) issue(seg + i, i, tile_row(seg + i));
       next_id = tile_row(seg + kAheadTiles);
       pend_row = tile_row(seg + kAheadTiles + 1);
+      step(seg, 0, false);
 #pragma clang loop unroll(disable)
-      for (int j = seg; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1));
+      for (int j = seg + 1; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1), true);
+      // the last tile's value product
+      __syncthreads();
+      const char* pl = lds + ((seg_end - 1 - seg) & (kStages - 1)) * kStageBytes;
+      v8 wb0[kWaves], va01[2];
+#pragma unroll
+      for (int g = 0; g < kWaves; ++g) wb0[g] = wload(g, 0);
+      va01[0] = vload(pl, 0, 0);
+      va01[1] = vload(pl, 1, 0);
+      floatx16 none;
+      pv(pl, std::integral_constant<bool, false>(), none, nullptr, wb0, va01);
     }
+    // the last steps' loads (no records: they only zero consumed stages)
+    // land before the workgroup moves on or ends
+    wait_vm_all();
   };
   run_tiles();
 
