@@ -592,7 +592,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   // between, so their vector work runs in the shadow of the
   // matrix instructions; they are returned packed in `pk`.
   auto pv = [&](const char* pb, auto soft, const floatx16& sa, t2* pk, const v8* wb0,
-                const v8* va01) __attribute__((always_inline)) {
+                const v8* va01, v8* wb1_out, v8* va67_out) __attribute__((always_inline)) {
     constexpr bool kSoft = decltype(soft)::value;
     // weight of score i: 2^(s * sl2 - m_ref) with s = sa[i]; pairs
     // are packed to the matrix input type. The output is normalised by the
@@ -613,34 +613,62 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       }
     };
     v8 wb[2][kWaves];
-    v8 va[3];
+    v8 va[4];
 #pragma unroll
     for (int g = 0; g < kWaves; ++g) wb[0][g] = wb0[g];
     va[0] = va01[0];
     va[1] = va01[1];
+    // with soft, groups 6 and 7 are left to the caller (their operands are
+    // returned): they fill the matrix unit across the step boundary
+    constexpr int kGroups = kSoft ? 6 : 8;
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
+    for (int n = 0; n < kGroups; ++n) {
       const int dt = n & 3, kk = n >> 2;
-      if (n + 2 < 8) va[(n + 2) % 3] = vload(pb, (n + 2) & 3, (n + 2) >> 2);
+      if (n + 2 < 8) va[(n + 2) & 3] = vload(pb, (n + 2) & 3, (n + 2) >> 2);
       if (n == 1)
 #pragma unroll
         for (int g = 0; g < kWaves; ++g) wb[1][g] = wload(g, 1);
 #pragma unroll
       for (int g = 0; g < kWaves; ++g) {
-        o[dt * 4 + g] = MT<T>::mfma(va[n % 3], wb[kk][g], o[dt * 4 + g]);
-        // one score's weight after every second matrix instruction
+        o[dt * 4 + g] = MT<T>::mfma(va[n & 3], wb[kk][g], o[dt * 4 + g]);
+        // the 16 weights spread over the 24 instructions
         if constexpr (kSoft) {
-          if ((g & 1) == 0) weight(2 * n + (g >> 1));
+          const int m = 4 * n + g;
+          if (m % 3 != 2) weight(m - m / 3);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       if constexpr (!kSoft) __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (kSoft) {
+#pragma unroll
+      for (int g = 0; g < kWaves; ++g) wb1_out[g] = wb[1][g];
+      va67_out[0] = va[6 & 3];
+      va67_out[1] = va[7 & 3];
+    }
+  };
+  // one group (latent tile 2 or 3 of token half 1) of a value product whose
+  // operands are already in registers
+  auto pv_group = [&](int dt, const v8& va, const v8* wb1, int gfrom, int gto)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = gfrom; g < gto; ++g) o[dt * 4 + g] = MT<T>::mfma(va, wb1[g], o[dt * 4 + g]);
   };
 
   // One step of the tile pipeline: tile j's score product, then the value
   // product of tile j - 1 (if `has_prev`) with tile j's softmax in between,
   // then tile j's weights go to sh_p once every wave is done reading it.
+  // group 7 of the previous step's value product, carried into this step
+  // (zero operands when there is none: the instructions then add zero)
+  v8 cw[kWaves], cv;
+  auto zero_carry = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int g = 0; g < kWaves; ++g)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cw[g][i] = (T)0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cv[i] = (T)0.f;
+  };
   auto step = [&](int j, int stage, bool has_prev) __attribute__((always_inline)) {
     wait_vm(min(kAheadTiles - 1, seg_end - 1 - j));
     __syncthreads();
@@ -685,6 +713,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     v8 kb[kRing];
 #pragma unroll
     for (int n = 0; n < kAhead; ++n) kb[n] = *kaddr(kstep(n));
+    // the carried group runs while the first key operands are in flight
+    pv_group(3, cv, cw, 0, kWaves);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < kKSteps; ++n) {
       const int k = kstep(n);
@@ -728,8 +759,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     __builtin_amdgcn_sched_barrier(0);
 
     t2 pk[8];
+    v8 va67[2];
     if (has_prev) {
-      pv(pb, std::integral_constant<bool, true>(), sacc, pk, wb0, va01);
+      pv(pb, std::integral_constant<bool, true>(), sacc, pk, wb0, va01, cw, va67);
     } else {
       // first tile of a segment: the weights alone (same arithmetic)
       float pf_even = 0.f;
@@ -748,10 +780,18 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       }
     }
     __syncthreads();  // every wave is done reading the previous weights
+    // the new weights go out between the instructions of group 6
 #pragma unroll
-    for (int j4 = 0; j4 < 4; ++j4)
+    for (int j4 = 0; j4 < 4; ++j4) {
       *(t4*)(sh_p + pst_off + (pchunk(j4, r32) << 4)) =
           __builtin_shufflevector(pk[2 * j4], pk[2 * j4 + 1], 0, 1, 2, 3);
+      if (has_prev) pv_group(2, va67[0], cw, j4, j4 + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (has_prev)
+      cv = va67[1];
+    else
+      zero_carry();
   };
 
   // Tiles run in segments of up to kIdCache: the row table is refilled and
@@ -767,6 +807,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
         if (seg + i < seg_end) issue(seg + i, i, tile_row(seg + i));
       next_id = tile_row(seg + kAheadTiles);
       pend_row = tile_row(seg + kAheadTiles + 1);
+      zero_carry();
       step(seg, 0, false);
 #pragma clang loop unroll(disable)
       for (int j = seg + 1; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1), true);
@@ -779,7 +820,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       va01[0] = vload(pl, 0, 0);
       va01[1] = vload(pl, 1, 0);
       floatx16 none;
-      pv(pl, std::integral_constant<bool, false>(), none, nullptr, wb0, va01);
+      pv_group(3, cv, cw, 0, kWaves);
+      pv(pl, std::integral_constant<bool, false>(), none, nullptr, wb0, va01, nullptr, nullptr);
     }
     // the last steps' loads (no records: they only zero consumed stages)
     // land before the workgroup moves on or ends
