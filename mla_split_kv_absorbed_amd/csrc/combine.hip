@@ -33,6 +33,13 @@ __device__ __forceinline__ void store8(T* p, const float* o) {
   *(typename Vec8<T>::v*)p = x;
 }
 
+// LSE of merged part i of a row (parts in index order, the local part last)
+__device__ __forceinline__ float part_lse(const CombineParams& c, int i, size_t row,
+                                          size_t rows) {
+  return i < c.P ? load_any(c.parts_lse, (size_t)i * rows + row, c.lse_dtype)
+                 : load_any(c.local_lse, row, c.lse_dtype);
+}
+
 template <typename TP, typename TO>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
   const int lane = threadIdx.x & 63;
@@ -41,29 +48,47 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
   if (row >= rows) return;
   const int np = c.P + (c.local_out ? 1 : 0);
 
+  // lane i holds the LSE of part i0 + i: the maximum and the weights take
+  // one load round trip for up to 64 parts
   float m = -INFINITY;
   bool nan_seen = false;
-  for (int i = 0; i < np; ++i) {
-    const float li = i < c.P ? load_any(c.parts_lse, (size_t)i * rows + row, c.lse_dtype)
-                             : load_any(c.local_lse, row, c.lse_dtype);
+  for (int i0 = 0; i0 < np; i0 += 64) {
+    const float li = i0 + lane < np ? part_lse(c, i0 + lane, row, rows) : -INFINITY;
     nan_seen |= isnan(li);
     m = fmaxf(m, li);
   }
+  m = wave_max(m);
+  nan_seen = __builtin_amdgcn_ballot_w64(nan_seen) != 0;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float z = 0.f;
   if (m != -INFINITY && !nan_seen) {
-    for (int i = 0; i < np; ++i) {
-      const float li = i < c.P ? load_any(c.parts_lse, (size_t)i * rows + row, c.lse_dtype)
-                               : load_any(c.local_lse, row, c.lse_dtype);
-      if (li == -INFINITY) continue;
-      const float w = expf(li - m);
-      z += w;
-      const TP* src = i < c.P ? (const TP*)c.parts_out + ((size_t)i * rows + row) * kDc
-                              : (const TP*)c.local_out + row * kDc;
-      float v[8];
-      load8<TP>(src + lane * 8, v);
+    for (int i0 = 0; i0 < np; i0 += 64) {
+      const int cnt = min(64, np - i0);
+      const float li = lane < cnt ? part_lse(c, i0 + lane, row, rows) : -INFINITY;
+      const float wl = li == -INFINITY ? 0.f : expf(li - m);
+      // parts in ascending order, 4 rows in flight
+      for (int i = 0; i < cnt; i += 4) {
+        float v[4][8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = fmaf(w, v[k], acc[k]);
+        for (int q = 0; q < 4; ++q) {
+          const int k = i0 + i + q;
+          if (i + q < cnt) {
+            const TP* src = k < c.P ? (const TP*)c.parts_out + ((size_t)k * rows + row) * kDc
+                                    : (const TP*)c.local_out + row * kDc;
+            load8<TP>(src + lane * 8, v[q]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float w = __shfl(wl, i + q, 64);
+          if (i + q < cnt) {
+            z += w;
+            if (w != 0.f)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[q][e], acc[e]);
+          }
+        }
+      }
     }
   }
   float o[8];

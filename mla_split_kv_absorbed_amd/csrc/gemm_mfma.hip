@@ -58,25 +58,36 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ 
   const int t0 = blockIdx.z * 32;
   const int r = lane & 31, hi = lane >> 5;
   const int t = t0 + r;
-  // B = q_nope^T: column t, 8 consecutive j per k step
+  // B = q_nope^T: column t, 8 consecutive j per k step; A = W_UK rows of the
+  // wave's two 32-row c tiles. Every operand is loaded before the first
+  // matrix instruction, so the wave pays one memory round trip.
+  // rows past Tn load the last valid row (no branch per load) and are zeroed
+  const int tl = min(t, Tn - 1);
   v8 b[kDn / 16];
 #pragma unroll
-  for (int k = 0; k < kDn / 16; ++k) {
-    if (t < Tn)
-      b[k] = *(const v8*)(qn + ((size_t)t * H + h) * kDn + k * 16 + hi * 8);
-    else
+  for (int k = 0; k < kDn / 16; ++k)
+    b[k] = *(const v8*)(qn + ((size_t)tl * H + h) * kDn + k * 16 + hi * 8);
+  if (t >= Tn)
+#pragma unroll
+    for (int k = 0; k < kDn / 16; ++k)
 #pragma unroll
       for (int i = 0; i < 8; ++i) b[k][i] = (T)0.f;
+  v8 a[2][kDn / 16];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const T* wr = wuk + ((size_t)h * kDc + c0 + ct * 32 + r) * kDn + hi * 8;
+#pragma unroll
+    for (int k = 0; k < kDn / 16; ++k) a[ct][k] = *(const v8*)(wr + k * 16);
   }
+  __builtin_amdgcn_sched_barrier(0);  // all loads issued before the first product
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct) {
     const int c = c0 + ct * 32;
-    const T* wr = wuk + ((size_t)h * kDc + c + r) * kDn + hi * 8;
     floatx16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < kDn / 16; ++k) acc = GT<T>::mfma(*(const v8*)(wr + k * 16), b[k], acc);
+    for (int k = 0; k < kDn / 16; ++k) acc = GT<T>::mfma(a[ct][k], b[k], acc);
     if (t < Tn) {
       T* dst = ql + ((size_t)t * H + h) * kDc + c + 4 * hi;
 #pragma unroll
@@ -91,30 +102,52 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// V-up: grid (H, 2 halves of v, ceil(T/32)), 2 waves, each wave one 32-column
-// v tile of one 32-token block; W_UV[h][:, 64-column half] staged in LDS.
+// V-up: grid (H, 2 halves of v, ceil(T/32)), 4 waves. All 4 waves stage
+// W_UV[h][:, 64-column half] in LDS (every load issued before the first LDS
+// write, so the block pays one memory round trip); waves 0 and 1 then each
+// compute one 32-column v tile of one 32-token block with their x operands
+// (all 32 k steps) already in registers.
 // ---------------------------------------------------------------------------
 constexpr int kVupCols = 64;
 constexpr int kVupRow = kVupCols * 2 + 32;  // bytes per LDS row (padded)
+constexpr int kVupThreads = 256;
+constexpr int kVupChunks = kDc * kVupCols * 2 / 16 / kVupThreads;  // 16-byte chunks per thread
 
 template <typename T>
-__global__ __launch_bounds__(128) void vup_mfma_kernel(const T* __restrict__ x,
-                                                       const T* __restrict__ wuv,
-                                                       T* __restrict__ out, int Tn, int H) {
+__global__ __launch_bounds__(kVupThreads) void vup_mfma_kernel(const T* __restrict__ x,
+                                                               const T* __restrict__ wuv,
+                                                               T* __restrict__ out, int Tn, int H) {
   typedef typename GT<T>::v8 v8;
   __shared__ __attribute__((aligned(16))) char ws[kDc * kVupRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x, vh = blockIdx.y * kVupCols;
   const int t0 = blockIdx.z * 32;
-  // stage W_UV[h][c][vh : vh+64]: 512 rows x 128 B, 8 x 16 B per row
-  const T* wsrc = wuv + (size_t)h * kDc * kDv + vh;
-  for (int i = tid; i < kDc * 8; i += 128) {
-    const int c = i >> 3, q = i & 7;
-    *(v8*)(ws + c * kVupRow + q * 16) = *(const v8*)(wsrc + (size_t)c * kDv + q * 8);
-  }
   const int r = lane & 31, hi = lane >> 5;
   const int t = t0 + r;
+  // W_UV[h][c][vh : vh+64]: 512 rows x 128 B = 4096 chunks of 16 B
+  const T* wsrc = wuv + (size_t)h * kDc * kDv + vh;
+  v8 st[kVupChunks];
+#pragma unroll
+  for (int i = 0; i < kVupChunks; ++i) {
+    const int idx = tid + i * kVupThreads, c = idx >> 3, q = idx & 7;
+    st[i] = *(const v8*)(wsrc + (size_t)c * kDv + q * 8);
+  }
+  // x operand of waves 0 and 1: column t, 8 consecutive c per k step
+  // (rows past Tn load the last valid row, no branch per load; their
+  // results are never stored)
+  v8 b[kDc / 16];
+  if (wave < 2) {
+    const T* xr = x + ((size_t)min(t, Tn - 1) * H + h) * kDc + hi * 8;
+#pragma unroll
+    for (int k = 0; k < kDc / 16; ++k) b[k] = *(const v8*)(xr + k * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < kVupChunks; ++i) {
+    const int idx = tid + i * kVupThreads, c = idx >> 3, q = idx & 7;
+    *(v8*)(ws + c * kVupRow + q * 16) = st[i];
+  }
   __syncthreads();
+  if (wave >= 2) return;
   // A = W^T (rows v, k = c) by transposed reads: 16-lane block g16 covers
   // v 16(g16&1)..+15 and c rows 8(g16>>1).. of each 16-wide k step
   const int j16 = lane & 15, g16 = lane >> 4;
@@ -123,21 +156,14 @@ __global__ __launch_bounds__(128) void vup_mfma_kernel(const T* __restrict__ x,
   floatx16 acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const T* xr = x + ((size_t)t * H + h) * kDc + hi * 8;
-#pragma unroll 8
-  for (int k = 0; k < kDc / 16; ++k) {
-    v8 b;
-    if (t < Tn)
-      b = *(const v8*)(xr + k * 16);
-    else
 #pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = (T)0.f;
+  for (int k = 0; k < kDc / 16; ++k) {
     const char* a0 = ws + a_off + k * 16 * kVupRow;
     const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)a0);
     const shortx4 h4 =
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + 4 * kVupRow));
     const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
-    acc = GT<T>::mfma(a, b, acc);
+    acc = GT<T>::mfma(a, b[k], acc);
   }
   if (t < Tn) {
     T* dst = out + ((size_t)t * H + h) * kDv + vh + wave * 32 + 4 * hi;
@@ -150,6 +176,8 @@ __global__ __launch_bounds__(128) void vup_mfma_kernel(const T* __restrict__ x,
     }
   }
 }
+
+static_assert(kVupChunks * kVupThreads * 16 == kDc * kVupCols * 2, "V-up staging split");
 
 hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int Tn, int H, int dt,
                               hipStream_t st) {
@@ -167,10 +195,10 @@ hipError_t launch_vup_mfma(const void* x, const void* w, void* out, int Tn, int 
                            hipStream_t st) {
   dim3 g(H, kDv / kVupCols, (Tn + 31) / 32);
   if (dt == MLA_BF16)
-    hipLaunchKernelGGL(vup_mfma_kernel<bf16>, g, dim3(128), 0, st, (const bf16*)x,
+    hipLaunchKernelGGL(vup_mfma_kernel<bf16>, g, dim3(kVupThreads), 0, st, (const bf16*)x,
                        (const bf16*)w, (bf16*)out, Tn, H);
   else
-    hipLaunchKernelGGL(vup_mfma_kernel<f16>, g, dim3(128), 0, st, (const f16*)x,
+    hipLaunchKernelGGL(vup_mfma_kernel<f16>, g, dim3(kVupThreads), 0, st, (const f16*)x,
                        (const f16*)w, (f16*)out, Tn, H);
   return hipGetLastError();
 }

@@ -1024,6 +1024,8 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
     hipLaunchKernelGGL(partial_mfma_kernel<f16>, grid, dim3(256), 0, st, mp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // no sub-splits requested: every range is written directly, nothing to merge
+  if (pp_in.num_splits == 1) return hipSuccess;
   // one wave per merged row: at most min(U, groups) split units (a split
   // unit has more tiles than a chunk), capped; the kernel strides beyond
   const size_t split_units = pp_in.num_splits > 1

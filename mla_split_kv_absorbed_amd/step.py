@@ -16,6 +16,10 @@ import torch
 from . import _lib as L
 from .workloads import D_C, D_V, Workload
 
+# workgroups one partial-attention call aims to spread over (the kernel
+# planner's target; one per compute unit)
+TARGET_GROUPS = 256
+
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
@@ -24,6 +28,18 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     if dtype == "bf16":
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(device)
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def split_hint(range_start: np.ndarray, range_end: np.ndarray, S: int) -> int:
+    """Sub-split hint for mla_decode_partial from the host-side ranges: 1 (no
+    sub-splits) when every range has the same length and there are at least
+    as many (range, query) units as the kernel's target workgroup count, so
+    cutting ranges cannot improve the balance; 0 (let the kernel plan)
+    otherwise."""
+    lens = np.asarray(range_end, np.int64) - np.asarray(range_start, np.int64)
+    if lens.size and lens.min() == lens.max() and lens.size * S >= TARGET_GROUPS:
+        return 1
+    return 0
 
 
 class DecodeStep:
@@ -62,6 +78,9 @@ class DecodeStep:
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H, D_V), dtype=self.dt, device=dev)
 
+        if num_splits == 0:
+            num_splits = split_hint(w.range_start, w.range_end, S)
+        self.num_splits = num_splits
         kw = dict(B=B, S=S, H=H, scale=sp.scale, num_splits=num_splits, flags=flags)
         if sp.block_size > 0:
             kw.update(block_table=self.block_table, block_size=sp.block_size,

@@ -73,3 +73,20 @@ def test_full_size_shapes_without_drawing_cache():
     r = np.random.Generator(np.random.PCG64(1004))
     L = W.draw_lengths(r, W.SPECS[4])
     assert L.min() >= 512 and L.max() <= 8192 and len(L) == 128
+
+
+def test_split_hint_policy():
+    """Host-side sub-split hint: no sub-splits only when every range has the
+    same length and the (range, query) units already fill the target
+    workgroup count."""
+    import numpy as np
+    from mla_split_kv_absorbed_amd.step import TARGET_GROUPS, split_hint
+    st = np.zeros((8, 32), np.int32)
+    en = np.full((8, 32), 4096, np.int32)
+    assert split_hint(st, en, 1) == 1                      # 256 equal units
+    assert split_hint(st[:1], en[:1], 1) == 0              # 32 units: let the kernel split
+    en2 = en.copy()
+    en2[0, 0] = 100
+    assert split_hint(st, en2, 1) == 0                     # ragged
+    assert split_hint(st[:4], en[:4], 2) == 1              # 128 units x 2 queries
+    assert TARGET_GROUPS == 256
