@@ -204,21 +204,41 @@ __device__ __forceinline__ int unit_chunks(int nt, int c, int hint) {
   return max(1, (nt + c - 1) / c);
 }
 
-// block-wide exclusive scan of one int per thread (256 threads)
-__device__ __forceinline__ int block_excl_scan(int v, int* sh, int& total) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    int x = tid >= o ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += x;
-    __syncthreads();
+// Block-wide exclusive scans over the 256 threads: prefix sums within each
+// wave by shuffles, then one LDS exchange of the 4 wave totals (2 barriers
+// per call). `sh` holds at least 4 * N ints.
+template <int N>
+__device__ __forceinline__ void block_excl_scan(const int (&v)[N], int* sh, int (&base)[N],
+                                                int (&total)[N]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) inc[k] = v[k];
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const int x = __shfl_up(inc[k], o, 64);
+      if (lane >= o) inc[k] += x;
+    }
   }
-  total = sh[255];
-  int r = sh[tid] - v;
+  if (lane == 63)
+#pragma unroll
+    for (int k = 0; k < N; ++k) sh[wave * N + k] = inc[k];
   __syncthreads();
-  return r;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int t = sh[w * N + k];
+      before += w < wave ? t : 0;
+      all += t;
+    }
+    base[k] = before + inc[k] - v[k];
+    total[k] = all;
+  }
+  __syncthreads();
 }
 
 struct Plan {
@@ -233,47 +253,65 @@ struct Found {
   int u, tb, te, slot, nsplit, split_idx;
 };
 
+// units per thread whose ranges stay in registers through the plan
+constexpr int kPlanCache = 4;
+
 __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Found* found, int* sh) {
   const int tid = threadIdx.x;
   const int U = pp.P * pp.B;
   const int per = (U + 255) / 256;
   const int u0 = min(U, tid * per), u1 = min(U, u0 + per);
+  // this thread's units: the first kPlanCache are loaded once
+  Unit uc[kPlanCache];
+#pragma unroll
+  for (int i = 0; i < kPlanCache; ++i) {
+    uc[i].nt = 0;
+    if (u0 + i < u1) uc[i] = load_unit(pp, u0 + i);
+  }
+  auto unit_at = [&](int i) __attribute__((always_inline)) -> Unit {
+    if (i < kPlanCache) {
+      Unit x = uc[0];
+#pragma unroll
+      for (int k = 1; k < kPlanCache; ++k)
+        if (i == k) x = uc[k];
+      return x;
+    }
+    return load_unit(pp, u0 + i);
+  };
   long long my_tiles = 0;
-  for (int u = u0; u < u1; ++u) my_tiles += load_unit(pp, u).nt;
+  for (int i = 0; i < u1 - u0; ++i) my_tiles += unit_at(i).nt;
   // total tiles (fits in int for any addressable cache)
-  int total;
-  block_excl_scan((int)my_tiles, sh, total);
+  int tv[1] = {(int)my_tiles}, tb_[1], tt[1];
+  block_excl_scan<1>(tv, sh, tb_, tt);
+  const int total = tt[0];
   Plan pl;
   const long long want_groups = kTargetGroups;
   long long c = ((long long)total * pp.S + want_groups - 1) / want_groups;
   pl.chunk_tiles = (int)max((long long)kMinChunkTiles, c);
-  int my_chunks = 0, my_slots = 0, my_splits = 0;
-  for (int u = u0; u < u1; ++u) {
-    const Unit x = load_unit(pp, u);
-    const int n = unit_chunks(x.nt, pl.chunk_tiles, pp.num_splits);
-    my_chunks += n;
+  int mv[3] = {0, 0, 0};  // chunks, split slots, split units of this thread
+  for (int i = 0; i < u1 - u0; ++i) {
+    const int n = unit_chunks(unit_at(i).nt, pl.chunk_tiles, pp.num_splits);
+    mv[0] += n;
     if (n > 1) {
-      my_slots += n;
-      my_splits += 1;
+      mv[1] += n;
+      mv[2] += 1;
     }
   }
-  int tot_chunks, tot_slots, tot_splits;
-  int cbase = block_excl_scan(my_chunks, sh, tot_chunks);
-  int sbase = block_excl_scan(my_slots, sh, tot_slots);
-  int pbase = block_excl_scan(my_splits, sh, tot_splits);
-  pl.nchunks = tot_chunks;
-  pl.nsplit_units = tot_splits;
-  if (want >= 0 && want >= cbase && want < cbase + my_chunks) {
-    int off = cbase, soff = sbase, poff = pbase;
-    for (int u = u0; u < u1; ++u) {
-      const Unit x = load_unit(pp, u);
+  int mb[3], mt[3];
+  block_excl_scan<3>(mv, sh, mb, mt);
+  pl.nchunks = mt[0];
+  pl.nsplit_units = mt[2];
+  if (want >= 0 && want >= mb[0] && want < mb[0] + mv[0]) {
+    int off = mb[0], soff = mb[1], poff = mb[2];
+    for (int i = 0; i < u1 - u0; ++i) {
+      const Unit x = unit_at(i);
       const int n = unit_chunks(x.nt, pl.chunk_tiles, pp.num_splits);
       if (want < off + n) {
-        const int i = want - off;
-        found->u = u;
-        found->tb = (int)((long long)i * x.nt / n);
-        found->te = (int)((long long)(i + 1) * x.nt / n);
-        found->slot = n > 1 ? soff + i : -1;
+        const int k = want - off;
+        found->u = u0 + i;
+        found->tb = (int)((long long)k * x.nt / n);
+        found->te = (int)((long long)(k + 1) * x.nt / n);
+        found->slot = n > 1 ? soff + k : -1;
         found->nsplit = n;
         found->split_idx = n > 1 ? poff : -1;
         break;
