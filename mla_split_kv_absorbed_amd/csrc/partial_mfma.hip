@@ -256,6 +256,19 @@ struct Found {
 // units per thread whose ranges stay in registers through the plan
 constexpr int kPlanCache = 4;
 
+// Chunk ids are handed out longest chunks first: chunks fall into 8 length
+// buckets of the chunk size, bucket by bucket from the longest, in unit order
+// within a bucket (one block scan, the same order in every workgroup), so
+// the in-order dispatch of workgroups places long chunks early on ragged
+// batches.
+constexpr int kBuckets = 8;
+
+__device__ __forceinline__ int len_bucket(int len, int c) {
+  // len <= c + 1 < 2^27 tiles, so 8 len fits in 32 bits; a uniform bucket
+  // set (equal chunks) skips the division
+  return len >= c ? kBuckets - 1 : min(kBuckets - 1, (unsigned)len * kBuckets / (unsigned)(c + 1));
+}
+
 __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Found* found, int* sh) {
   const int tid = threadIdx.x;
   const int U = pp.P * pp.B;
@@ -286,27 +299,55 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
   const int total = tt[0];
   Plan pl;
   const long long want_groups = kTargetGroups;
-  long long c = ((long long)total * pp.S + want_groups - 1) / want_groups;
-  pl.chunk_tiles = (int)max((long long)kMinChunkTiles, c);
-  int mv[3] = {0, 0, 0};  // chunks, split slots, split units of this thread
+  const long long cw = ((long long)total * pp.S + want_groups - 1) / want_groups;
+  pl.chunk_tiles = (int)max((long long)kMinChunkTiles, cw);
+  const int c = pl.chunk_tiles;
+  // per bucket chunk counts of this thread, plus all chunks, split slots and
+  // split units
+  int mv[kBuckets + 3];
+#pragma unroll
+  for (int k = 0; k < kBuckets + 3; ++k) mv[k] = 0;
   for (int i = 0; i < u1 - u0; ++i) {
-    const int n = unit_chunks(unit_at(i).nt, pl.chunk_tiles, pp.num_splits);
-    mv[0] += n;
+    const Unit x = unit_at(i);
+    const int n = unit_chunks(x.nt, c, pp.num_splits);
+    const int bk = len_bucket((x.nt + n - 1) / n, c);
+#pragma unroll
+    for (int k = 0; k < kBuckets; ++k)
+      if (bk == k) mv[k] += n;
+    mv[kBuckets] += n;
     if (n > 1) {
-      mv[1] += n;
-      mv[2] += 1;
+      mv[kBuckets + 1] += n;
+      mv[kBuckets + 2] += 1;
     }
   }
-  int mb[3], mt[3];
-  block_excl_scan<3>(mv, sh, mb, mt);
-  pl.nchunks = mt[0];
-  pl.nsplit_units = mt[2];
-  if (want >= 0 && want >= mb[0] && want < mb[0] + mv[0]) {
-    int off = mb[0], soff = mb[1], poff = mb[2];
+  int mb[kBuckets + 3], mt[kBuckets + 3];
+  block_excl_scan<kBuckets + 3>(mv, sh, mb, mt);
+  pl.nchunks = mt[kBuckets];
+  pl.nsplit_units = mt[kBuckets + 2];
+  if (want < 0 || want >= pl.nchunks) return pl;  // grid slack: nothing to find
+  // first chunk id of a bucket: the chunks of all longer buckets come first
+  int run[kBuckets];
+#pragma unroll
+  for (int k = 0; k < kBuckets; ++k) {
+    int above = 0;
+#pragma unroll
+    for (int k2 = k + 1; k2 < kBuckets; ++k2) above += mt[k2];
+    run[k] = above + mb[k];
+  }
+  {
+    int soff = mb[kBuckets + 1], poff = mb[kBuckets + 2];
     for (int i = 0; i < u1 - u0; ++i) {
       const Unit x = unit_at(i);
-      const int n = unit_chunks(x.nt, pl.chunk_tiles, pp.num_splits);
-      if (want < off + n) {
+      const int n = unit_chunks(x.nt, c, pp.num_splits);
+      const int bk = len_bucket((x.nt + n - 1) / n, c);
+      int off = run[0];
+#pragma unroll
+      for (int k = 1; k < kBuckets; ++k)
+        if (bk == k) off = run[k];
+#pragma unroll
+      for (int k = 0; k < kBuckets; ++k)
+        if (bk == k) run[k] += n;
+      if (want >= off && want < off + n) {
         const int k = want - off;
         found->u = u0 + i;
         found->tb = (int)((long long)k * x.nt / n);
@@ -316,7 +357,6 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
         found->split_idx = n > 1 ? poff : -1;
         break;
       }
-      off += n;
       if (n > 1) {
         soff += n;
         poff += 1;
