@@ -46,7 +46,8 @@ class DecodeStep:
     """Device-resident inputs, outputs and workspace of one decode step."""
 
     def __init__(self, w: Workload, device="cuda", part_lse_dtype: Optional[str] = None,
-                 num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None):
+                 num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None,
+                 side_stream: bool = False):
         sp = w.spec
         self.w = w
         self.dev = torch.device(device)
@@ -107,17 +108,41 @@ class DecodeStep:
         for a in [self.hist_args] + ([self.cur_args] if sp.current else []):
             a.workspace = self.workspace.data_ptr()
             a.workspace_bytes = self.workspace.numel()
+        # Current-chunk attention on a side stream, concurrent with the
+        # history partial (the study page's stream split). It gets its own
+        # workspace: a workspace belongs to one call until its stream has
+        # passed it. Every buffer it touches is owned by this object for its
+        # whole life, so no allocator stream bookkeeping is needed.
+        self.side = None
+        if side_stream and sp.current:
+            self.side = torch.cuda.Stream(device=dev)  # default priority
+            self.cur_workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
+            self.cur_args.workspace = self.cur_workspace.data_ptr()
+            self.cur_args.workspace_bytes = self.cur_workspace.numel()
+            self.ev_q = torch.cuda.Event()    # q_lat ready (main -> side)
+            self.ev_cur = torch.cuda.Event()  # current partial done (side -> main)
         # with a single part and no local part the partial already is the
         # merged latent; the combine is skipped
         self.skip_combine = (P == 1 and not sp.current and pdt == odt
                              and self.parts_lse.dtype == torch.float32)
 
     def run(self, stream=None):
+        main = stream if stream is not None else torch.cuda.current_stream(self.dev)
         if self.absorb:
-            L.mla_q_absorb(self.q_nope, self.w_uk, self.q_lat, stream)
-        L.mla_decode_partial(self.hist_args, stream)
-        if self.w.spec.current:
-            L.mla_decode_partial(self.cur_args, stream)
+            L.mla_q_absorb(self.q_nope, self.w_uk, self.q_lat, main)
+        if self.side is not None:
+            # side stream: after q_lat, before the combine
+            self.ev_q.record(main)
+            self.side.wait_event(self.ev_q)
+            L.mla_decode_partial(self.cur_args, self.side)
+            self.ev_cur.record(self.side)
+            L.mla_decode_partial(self.hist_args, main)
+            main.wait_event(self.ev_cur)
+        else:
+            L.mla_decode_partial(self.hist_args, main)
+            if self.w.spec.current:
+                L.mla_decode_partial(self.cur_args, main)
+        stream = main
         if self.skip_combine:
             x = self.parts_out[0]
         else:

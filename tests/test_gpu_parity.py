@@ -398,3 +398,27 @@ def test_vup_and_absorb(dt):
         else:
             # one rounding of the fp32 result to the storage type
             assert np.all(np.abs(got - ref) <= 2 * half_ulp(ref, dt) + 1e-4)
+
+
+@pytest.mark.parametrize("full", [False, True])
+def test_side_stream_matches_serial(full):
+    """The current-chunk partial on a side stream, ordered by events after
+    q-absorb and before the combine, gives bit for bit the step of the
+    serial order. Its outputs are poisoned with NaN on the main stream before
+    every run, so a combine that ran before the side stream finished (or a
+    side call that started before q_lat was written) would show."""
+    sp = W.SPECS[3] if full else W.spec(3, B=6, lengths=("uniform", 100, 1500))
+    w = W.make_workload(sp)
+    ser = DecodeStep(w)
+    ser.run()
+    side = DecodeStep(w, side_stream=True)
+    assert side.side is not None
+    torch.cuda.synchronize()
+    for _ in range(3):
+        side.cur_out.fill_(float("nan"))
+        side.cur_lse.fill_(float("nan"))
+        side.q_lat.fill_(float("nan"))
+        side.run()
+        torch.cuda.synchronize()
+        assert torch.equal(side.out, ser.out)
+        assert torch.equal(side.final_lse(), ser.final_lse())
