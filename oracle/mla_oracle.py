@@ -28,6 +28,13 @@ What it computes is the plain definition of the result, written out:
   partial (`latent_partial`: attention whose keys are [c_KV || k_R] and whose
   values are c_KV itself) are the plain definitions of what the library's
   q-absorb and partial-attention entry points return.
+* The decode prologue (`decode_prologue`): the step before the path. Rotary
+  position embedding of the query's rope part and of the new token's k_R
+  (`rope`: consecutive pairs rotated by pos * theta^(-2i/d_R), theta 10000;
+  the pages name the fused RoPE prologue but fix no variant, so the
+  original rotary formulation is the reading), q absorption, and the
+  append of the new token's [c_KV || rope(k_R)] row at its paged slot
+  (`cache_slot`).
 
 Readings where the pages are silent: natural-log LSE of the *scaled* scores;
 an empty key set gives output 0 and LSE -inf; the MTP current-window mask is
@@ -38,7 +45,10 @@ Pins (tests, CPU): brute-force loops without the max trick on tiny sizes, the
 library SDPA routine over the oracle's materialised K/V, the absorbed form
 (written only in the tests), split invariance of the combine, closed forms,
 extreme shifted parts, the causal-window equivalences, the pages' printed
-layout sizes, and planted-mistake checks.  No page prints an attention output
+layout sizes, rotary closed forms and the relative-position identity, the
+cache append read back through the block table, and planted-mistake
+checks. The rotary frequency schedule itself is the reading above (parity
+unpinned by the pages beyond the rotation's structure).  No page prints an attention output
 or LSE value, so the numeric values themselves rest on the textbook
 definition plus those checks.
 """
@@ -226,3 +236,70 @@ def latent_bytes_per_token(d_c: int, d_r: int, elem_bytes: int) -> int:
 def block_bytes(block_size: int, d_c: int, d_r: int, elem_bytes: int) -> int:
     """Bytes of one paged cache block of `block_size` tokens."""
     return block_size * latent_bytes_per_token(d_c, d_r, elem_bytes)
+
+
+# ----------------------------------------------------------------------------
+# the decode prologue: rotary position embedding, q absorption, cache append
+# ----------------------------------------------------------------------------
+
+def rope(x: np.ndarray, pos, theta: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding of the decoupled rope part (d_R values on the
+    last axis) at integer position(s) `pos` (broadcast against x[..., 0]).
+
+    The "MLA multi-GPU sharding" page calls k_R the small decoupled rotary
+    position vector and the "RTPLLM on K3" page (section 4.1) fuses the RoPE
+    transform into the attention prologue; neither fixes the variant. The
+    reading taken: the original rotary formulation, each consecutive pair
+    (x[2i], x[2i+1]) rotated by the angle pos * theta^(-2i/d_R):
+        y[2i]   = x[2i] cos(a_i) - x[2i+1] sin(a_i)
+        y[2i+1] = x[2i] sin(a_i) + x[2i+1] cos(a_i)
+    """
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    i = np.arange(d // 2, dtype=np.float64)
+    inv_freq = theta ** (-2.0 * i / d)
+    ang = np.asarray(pos, np.float64)[..., None] * inv_freq
+    c, s = np.cos(ang), np.sin(ang)
+    xe, xo = x[..., 0::2], x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = xe * c - xo * s
+    y[..., 1::2] = xe * s + xo * c
+    return y
+
+
+def cache_slot(b: int, pos: int, block_table: Optional[np.ndarray], block_size: int,
+               seq_stride: int) -> int:
+    """Cache row of logical token `pos` of sequence b: block_table[b][pos / bs]
+    * bs + pos % bs for a paged cache, b * seq_stride + pos for a contiguous
+    one (the paged layout of the "MLA multi-GPU sharding" page's block
+    sizes)."""
+    if block_size > 0:
+        return int(block_table[b, pos // block_size]) * block_size + pos % block_size
+    return b * seq_stride + pos
+
+
+def decode_prologue(q_nope: np.ndarray, q_pe: np.ndarray, w_uk: np.ndarray,
+                    kv_new: np.ndarray, positions: np.ndarray, cache_rows: np.ndarray,
+                    block_table: Optional[np.ndarray], block_size: int, seq_stride: int,
+                    B: int, S: int, d_c: int, theta: float = 10000.0):
+    """The step before the attention path, written out: for every new token
+    t = b * S + s at position positions[t],
+      q_lat[t]   = W_UK[h] . q_nope[t]            (absorption, per head)
+      q_rope[t]  = rope(q_pe[t], positions[t])    (per head)
+      cache row  = [c_KV(t) || rope(k_R(t), positions[t])]  appended at the
+                   token's slot (every other row unchanged).
+    cache_rows is the cache flattened to [rows][d_c + d_R]; a copy is
+    returned. The "RTPLLM on K3" page (sections 2.1 and 4.1): the input
+    projection yields the query's latent and rope parts and the compressed
+    latent that the cache stores; RoPE is applied in the fused prologue."""
+    q_lat = q_absorb(q_nope, w_uk)
+    pos = np.asarray(positions, np.int64)
+    q_rope = rope(q_pe, pos[:, None], theta)
+    new = np.array(cache_rows, np.float64, copy=True)
+    for b in range(B):
+        for s_ in range(S):
+            t = b * S + s_
+            r = cache_slot(b, int(pos[t]), block_table, block_size, seq_stride)
+            new[r, :d_c] = kv_new[t, :d_c]
+            new[r, d_c:] = rope(kv_new[t, d_c:], int(pos[t]), theta)
+    return q_lat, q_rope, new

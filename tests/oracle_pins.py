@@ -343,6 +343,101 @@ def pin_layout_sizes(mo):
     return bad
 
 
+# ---------------------------------------------------------------------------
+# the decode prologue: rotary embedding and cache append
+# ---------------------------------------------------------------------------
+
+def pin_rope_closed_forms(mo):
+    """Closed forms of the rotation: position 0 is the identity; a unit vector
+    in pair i at position p lands at (cos, sin) of p * theta^(-2i/d) (pair 0
+    has frequency 1, pair 1 of d = 4 has theta^(-1/2)); rotations by m then n
+    compose to m + n; each pair keeps its length."""
+    theta = 10000.0
+    bad = 0.0
+    x = _rng(71).standard_normal((5, 64))
+    bad = max(bad, np.abs(mo.rope(x, np.zeros(5)) - x).max())
+    for p in (1, 7, 1000, 32767):
+        y = mo.rope(np.array([1.0, 0.0]), p, theta)
+        bad = max(bad, abs(y[0] - math.cos(p)), abs(y[1] - math.sin(p)))
+        y = mo.rope(np.array([0.0, 0.0, 1.0, 0.0]), p, theta)
+        a = p * theta ** -0.5
+        bad = max(bad, abs(y[0]), abs(y[1]), abs(y[2] - math.cos(a)), abs(y[3] - math.sin(a)))
+        y = mo.rope(np.array([0.0, 1.0]), p, theta)
+        bad = max(bad, abs(y[0] + math.sin(p)), abs(y[1] - math.cos(p)))
+    m, n = np.array([3, 50, 9000]), np.array([11, 4, 123])
+    x = _rng(72).standard_normal((3, 64))
+    bad = max(bad, np.abs(mo.rope(mo.rope(x, m), n) - mo.rope(x, m + n)).max() / 10.0)
+    y = mo.rope(x, m)
+    bad = max(bad, np.abs(np.hypot(y[:, 0::2], y[:, 1::2]) - np.hypot(x[:, 0::2], x[:, 1::2])).max())
+    return bad
+
+
+def pin_rope_relative(mo):
+    """The defining property of rotary embedding: the dot product of a query
+    rotated to position m and a key rotated to position n depends only on
+    m - n."""
+    r = _rng(73)
+    q, k = r.standard_normal((4, 64)), r.standard_normal((4, 64))
+    bad = 0.0
+    for m, n in ((5, 2), (300, 17), (16000, 15990), (7, 7)):
+        a = np.einsum("ij,ij->i", mo.rope(q, np.full(4, m)), mo.rope(k, np.full(4, n)))
+        b = np.einsum("ij,ij->i", mo.rope(q, np.full(4, m - n)), k)
+        bad = max(bad, np.abs(a - b).max() / 64.0)
+    return bad
+
+
+def pin_cache_append(mo):
+    """Appending the new tokens through a paged block table: reading every
+    sequence back in logical order by gathering its blocks shows the new
+    rows (latent copied, rope part rotated) at their positions and every
+    other token unchanged; the same holds for a contiguous cache. The
+    absorbed query and rotated query rope part match their definitions."""
+    r = _rng(74)
+    B, S, H, bs, d_c, d_r, dn = 3, 2, 2, 4, 8, 4, 4
+    nb_per = 3
+    perm = r.permutation(B * nb_per + 2)  # two spare blocks
+    block_table = perm[:B * nb_per].reshape(B, nb_per).astype(np.int32)
+    cache = r.standard_normal((perm.size * bs, d_c + d_r))
+    T = B * S
+    kv_new = r.standard_normal((T, d_c + d_r))
+    positions = np.array([5, 6, 0, 1, 10, 11], np.int32)
+    q_nope, q_pe = r.standard_normal((T, H, dn)), r.standard_normal((T, H, d_r))
+    w_uk = r.standard_normal((H, d_c, dn))
+    ql, qr, new = mo.decode_prologue(q_nope, q_pe, w_uk, kv_new, positions, cache,
+                                     block_table, bs, 0, B, S, d_c)
+    bad = 0.0
+    blocks_old = cache.reshape(-1, bs, d_c + d_r)
+    blocks_new = new.reshape(-1, bs, d_c + d_r)
+    for b in range(B):
+        seq_old = blocks_old[block_table[b]].reshape(-1, d_c + d_r)
+        seq_new = blocks_new[block_table[b]].reshape(-1, d_c + d_r)
+        touched = set()
+        for s_ in range(S):
+            t = b * S + s_
+            p = int(positions[t])
+            touched.add(p)
+            bad = max(bad, np.abs(seq_new[p, :d_c] - kv_new[t, :d_c]).max())
+            want = mo.rope(kv_new[t, d_c:], p)
+            bad = max(bad, np.abs(seq_new[p, d_c:] - want).max())
+        for p in range(seq_old.shape[0]):
+            if p not in touched:
+                bad = max(bad, np.abs(seq_new[p] - seq_old[p]).max())
+    spare = blocks_new[perm[B * nb_per:]]
+    bad = max(bad, np.abs(spare - blocks_old[perm[B * nb_per:]]).max())
+    # contiguous cache: sequence b occupies rows [b * stride, (b + 1) * stride)
+    stride = 16
+    cc = r.standard_normal((B * stride, d_c + d_r))
+    _, _, cn = mo.decode_prologue(q_nope, q_pe, w_uk, kv_new, positions, cc, None, 0, stride,
+                                  B, S, d_c)
+    diff = np.argwhere(np.any(cn != cc, axis=1)).ravel().tolist()
+    want_rows = sorted(b * stride + int(positions[b * S + s_]) for b in range(B) for s_ in range(S))
+    bad = max(bad, 0.0 if diff == want_rows else 1.0)
+    for h in range(H):
+        bad = max(bad, np.abs(ql[:, h] - np.einsum("cj,tj->tc", w_uk[h], q_nope[:, h])).max())
+    bad = max(bad, np.abs(qr - mo.rope(q_pe, positions[:, None])).max())
+    return bad
+
+
 PINS = {
     "brute_force": (pin_brute_force, 1e-12),
     "sdpa": (pin_sdpa, 1e-12),
@@ -353,4 +448,7 @@ PINS = {
     "causal_window": (pin_causal_window, 1e-12),
     "vup_bmm": (pin_vup_bmm, 1e-10),
     "layout_sizes": (pin_layout_sizes, 0.0),
+    "rope_closed_forms": (pin_rope_closed_forms, 1e-9),
+    "rope_relative": (pin_rope_relative, 1e-9),
+    "cache_append": (pin_cache_append, 1e-12),
 }

@@ -24,6 +24,8 @@ def _failing_pins(module):
                 err = fn(module)
             if not (err <= tol):
                 failed.append(name)
+        except (NameError, AttributeError, TypeError):
+            raise  # a broken harness or mutant, not a caught mistake
         except Exception:
             failed.append(name)
     return failed
@@ -33,6 +35,9 @@ def _mutant(**repl):
     m = types.ModuleType("oracle_mutant")
     m.__dict__.update({k: v for k, v in mo.__dict__.items() if not k.startswith("__")})
     m.__dict__["__builtins__"] = mo.__dict__["__builtins__"]
+    # the unmodified functions that mutant wrappers delegate to
+    m.__dict__.update(ORIG_ATTEND=mo.attend, ORIG_ROPE=mo.rope, ORIG_SLOT=mo.cache_slot, np=np,
+                      math=math)
     for k, v in repl.items():
         if callable(v) and not isinstance(v, type):
             v = types.FunctionType(v.__code__, m.__dict__, k, v.__defaults__, v.__closure__)
@@ -95,6 +100,40 @@ def _attend_noscale(q, K, V, scale, visible=None):
 
 ORIG_ATTEND = mo.attend
 
+
+def _rope_sign(x, pos, theta=10000.0):
+    return ORIG_ROPE(x, -np.asarray(pos), theta)
+
+
+def _rope_half_split(x, pos, theta=10000.0):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.asarray(pos, np.float64)[..., None] * theta ** (-2.0 * i / d)
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :d // 2], x[..., d // 2:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def _rope_freq(x, pos, theta=10000.0):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    i = np.arange(d // 2, dtype=np.float64)
+    ang = np.asarray(pos, np.float64)[..., None] * theta ** (-1.0 * i / d)
+    c, s = np.cos(ang), np.sin(ang)
+    y = np.empty_like(x)
+    y[..., 0::2] = x[..., 0::2] * c - x[..., 1::2] * s
+    y[..., 1::2] = x[..., 0::2] * s + x[..., 1::2] * c
+    return y
+
+
+def _slot_off_by_one(b, pos, block_table, block_size, seq_stride):
+    return ORIG_SLOT(b, pos + 1, block_table, block_size, seq_stride)
+
+
+ORIG_ROPE = mo.rope
+ORIG_SLOT = mo.cache_slot
+
 MUTANTS = {
     "dropped rope key": dict(materialize_kv=_kv_no_rope),
     "W_UK/W_UV swapped": dict(materialize_kv=_kv_swapped),
@@ -105,13 +144,18 @@ MUTANTS = {
     "q_absorb wrong head": dict(q_absorb=_absorb_wrong_head),
     "lse in log2": dict(attend=_attend_log2),
     "scale dropped": dict(attend=_attend_noscale),
+    "rope rotates the wrong way": dict(rope=_rope_sign),
+    "rope pairs halves": dict(rope=_rope_half_split),
+    "rope frequency exponent": dict(rope=_rope_freq),
+    "cache append off by one": dict(cache_slot=_slot_off_by_one),
 }
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name):
     repl = dict(MUTANTS[name])
-    # wrappers around the original attend must stay bound to the original
+    # wrappers delegate to the unmodified functions (ORIG_*), which stay
+    # bound to the original oracle module
     m = _mutant(**repl)
     failed = _failing_pins(m)
     assert failed, f"planted mistake '{name}' passed every pin"
