@@ -178,6 +178,56 @@ int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int par
  *   x [T][H][512], w_uv [H][512][128], out [T][H][128] == [T][H*128]. */
 int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype, void* stream);
 
+/*
+ * Arguments of mla_decode_prologue: the step before the attention path for
+ * T = B*S new tokens (t = b*S + s, the s-th new token of sequence b).
+ *   q_nope [T][H][128], q_pe [T][H][64] (before rotation),
+ *   w_uk [H][512][128], kv_new [T][576] (the new tokens' c_KV, then their
+ *   k_R before rotation), all `dtype`.
+ *   positions int32 [T] (DEVICE): the logical position of each new token in
+ *   its sequence, used as the rotation angle and as its cache slot.
+ *   rope_theta > 0: rotary base.
+ *   Cache: the same layout as mla_partial_args (paged: kv, block_table
+ *   [B][max_blocks], block_size > 0, num_blocks; contiguous: block_table
+ *   NULL, block_size 0, kv_seq_stride rows per sequence).
+ * Outputs: q_lat [T][H][512], q_rope [T][H][64] (rotated), and the cache
+ *   row of every new token. A token whose position is negative or whose
+ *   slot lies outside the block table, the cache or the contiguous stride is
+ *   not written (detected on the device; nothing is written out of bounds).
+ *   Only the new tokens' rows are written; kv_new must not overlap the cache.
+ */
+typedef struct mla_prologue_args {
+  const void* q_nope;
+  const void* q_pe;
+  const void* w_uk;
+  const void* kv_new;
+  const int32_t* positions;
+  int dtype;
+  int B, S, H;
+  float rope_theta;
+  void* kv;
+  const int32_t* block_table;
+  int block_size, max_blocks, num_blocks;
+  int kv_seq_stride;
+  void* q_lat;
+  void* q_rope;
+} mla_prologue_args;
+
+/* Fused decode prologue ("RTPLLM on K3" page: section 2.1, the input
+ * projection yields the query's latent and rope parts and the compressed
+ * latent the cache stores; section 4.1, the RoPE transform fused into one
+ * kernel with the latent handling):
+ *   q_lat[t][h]  = W_UK[h] . q_nope[t][h]                (as mla_q_absorb)
+ *   q_rope[t][h] = rope(q_pe[t][h], positions[t])
+ *   cache row of token t at position pos = positions[t] of sequence b:
+ *     [kv_new[t][0:512] || rope(kv_new[t][512:576], pos)]
+ * rope rotates each consecutive pair (x[2i], x[2i+1]) of the 64 rope values
+ * by the angle pos * rope_theta^(-2i/64) (x[2i] cos - x[2i+1] sin,
+ * x[2i] sin + x[2i+1] cos); the angle is formed in double precision.
+ * bf16 / fp16 run as one kernel (matrix-core absorption with the rotation
+ * and append in the same launch); fp32 as two. */
+int mla_decode_prologue(const mla_prologue_args* a, void* stream);
+
 /* Human-readable text for a status code (static string, never NULL). */
 const char* mla_status_string(int status);
 

@@ -54,6 +54,19 @@ class PartialArgs(ctypes.Structure):
     ]
 
 
+class PrologueArgs(ctypes.Structure):
+    _fields_ = [
+        ("q_nope", ctypes.c_void_p), ("q_pe", ctypes.c_void_p), ("w_uk", ctypes.c_void_p),
+        ("kv_new", ctypes.c_void_p), ("positions", ctypes.c_void_p), ("dtype", ctypes.c_int),
+        ("B", ctypes.c_int), ("S", ctypes.c_int), ("H", ctypes.c_int),
+        ("rope_theta", ctypes.c_float),
+        ("kv", ctypes.c_void_p), ("block_table", ctypes.c_void_p),
+        ("block_size", ctypes.c_int), ("max_blocks", ctypes.c_int), ("num_blocks", ctypes.c_int),
+        ("kv_seq_stride", ctypes.c_int),
+        ("q_lat", ctypes.c_void_p), ("q_rope", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -79,6 +92,8 @@ def lib():
         L.mla_vup.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         L.mla_lse_combine.restype = ci
         L.mla_lse_combine.argtypes = [vp, vp, ci, ci, ci, vp, vp, ci, ci, vp, ci, vp, vp]
+        L.mla_decode_prologue.restype = ci
+        L.mla_decode_prologue.argtypes = [ctypes.POINTER(PrologueArgs), vp]
         _lib = L
     return _lib
 
@@ -170,3 +185,25 @@ def mla_lse_combine(parts_out, parts_lse, out, lse_out=None, local_out=None, loc
                                  DT_CODE[refl.dtype], _ptr(local_out), _ptr(local_lse), T, H,
                                  _ptr(out), DT_CODE[out.dtype], _ptr(lse_out), _stream(stream)),
            "mla_lse_combine")
+
+
+def prologue_args(q_nope, q_pe, w_uk, kv_new, positions, kv, q_lat, q_rope, *, B, S,
+                  rope_theta=10000.0, block_table=None, block_size=0, num_blocks=0,
+                  kv_seq_stride=0) -> PrologueArgs:
+    a = PrologueArgs()
+    a.q_nope, a.q_pe, a.w_uk = _ptr(q_nope), _ptr(q_pe), _ptr(w_uk)
+    a.kv_new, a.positions = _ptr(kv_new), _ptr(positions)
+    a.dtype = DT_CODE[q_nope.dtype]
+    a.B, a.S, a.H = B, S, q_nope.shape[1]
+    a.rope_theta = rope_theta
+    a.kv, a.block_table = _ptr(kv), _ptr(block_table)
+    a.block_size = block_size
+    a.max_blocks = block_table.shape[1] if block_table is not None else 0
+    a.num_blocks = num_blocks
+    a.kv_seq_stride = kv_seq_stride
+    a.q_lat, a.q_rope = _ptr(q_lat), _ptr(q_rope)
+    return a
+
+
+def mla_decode_prologue(a: PrologueArgs, stream=None):
+    _check(lib().mla_decode_prologue(ctypes.byref(a), _stream(stream)), "mla_decode_prologue")

@@ -8,6 +8,8 @@
 #include "common.h"
 #include "kernels.h"
 
+#include <cmath>
+
 using namespace mla;
 
 namespace {
@@ -224,6 +226,67 @@ int mla_q_absorb(const void* q_nope, const void* w_uk, void* q_lat, int T, int H
   hipError_t he = dtype == MLA_F32
                     ? launch_absorb_simple(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream)
                     : launch_absorb_mfma(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream);
+  return he == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int mla_decode_prologue(const mla_prologue_args* a, void* stream) {
+  if (!a) return MLA_ERR_NULL;
+  if (!a->q_nope || !a->q_pe || !a->w_uk || !a->kv_new || !a->positions || !a->kv ||
+      !a->q_lat || !a->q_rope)
+    return MLA_ERR_NULL;
+  if (!valid_dtype(a->dtype)) return MLA_ERR_DTYPE;
+  if (a->B < 1 || a->S < 1 || a->H < 1 || a->H > 65535) return MLA_ERR_SHAPE;
+  if ((long long)a->B * a->S > (1 << 30)) return MLA_ERR_SHAPE;
+  if (!(a->rope_theta > 0.f) || !std::isfinite(a->rope_theta)) return MLA_ERR_RANGE;
+  size_t cache_rows;
+  if (a->block_size > 0) {
+    if (!a->block_table) return MLA_ERR_NULL;
+    if (a->max_blocks < 1 || a->num_blocks < 1) return MLA_ERR_SHAPE;
+    cache_rows = (size_t)a->num_blocks * a->block_size;
+  } else {
+    if (a->block_size < 0 || a->block_table) return MLA_ERR_SHAPE;
+    if (a->kv_seq_stride < 1) return MLA_ERR_SHAPE;
+    cache_rows = (size_t)a->B * a->kv_seq_stride;
+  }
+  const size_t T = (size_t)a->B * a->S, H = a->H, e = elem_bytes(a->dtype);
+  Extent ins[7] = {{a->q_nope, T * H * kDn * e},
+                   {a->q_pe, T * H * kDr * e},
+                   {a->w_uk, H * kDc * kDn * e},
+                   {a->kv_new, T * kRow * e},
+                   {a->positions, T * 4},
+                   {a->block_table, a->block_size > 0 ? (size_t)a->B * a->max_blocks * 4 : 0},
+                   {a->kv, cache_rows * kRow * e}};
+  Extent outs[3] = {{a->q_lat, T * H * kDc * e}, {a->q_rope, T * H * kDr * e},
+                    {a->kv, cache_rows * kRow * e}};
+  // the cache is written in place: check it against every input but itself
+  if (any_overlap(outs, 2, ins, 7) || any_overlap(outs + 2, 1, ins, 6)) return MLA_ERR_ALIAS;
+  PrologueParams pp;
+  pp.q_nope = a->q_nope;
+  pp.q_pe = a->q_pe;
+  pp.w_uk = a->w_uk;
+  pp.kv_new = a->kv_new;
+  pp.positions = a->positions;
+  pp.B = a->B;
+  pp.S = a->S;
+  pp.H = a->H;
+  pp.T = (int)T;
+  pp.log2_theta = std::log2((double)a->rope_theta);
+  pp.kv = a->kv;
+  pp.block_table = a->block_size > 0 ? a->block_table : nullptr;
+  pp.block_size = a->block_size;
+  pp.max_blocks = a->max_blocks;
+  pp.num_blocks = a->num_blocks;
+  pp.kv_seq_stride = a->kv_seq_stride;
+  pp.q_lat = a->q_lat;
+  pp.q_rope = a->q_rope;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t he;
+  if (a->dtype == MLA_F32) {
+    he = launch_absorb_simple(a->q_nope, a->w_uk, a->q_lat, (int)T, a->H, a->dtype, st);
+    if (he == hipSuccess) he = launch_rope_append(pp, a->dtype, st);
+  } else {
+    he = launch_prologue_mfma(pp, a->dtype, st);
+  }
   return he == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 

@@ -15,6 +15,7 @@
 // each lane, so every store is one 8-byte write.
 #include "common.h"
 #include "kernels.h"
+#include "prologue.h"
 
 namespace mla {
 
@@ -48,9 +49,8 @@ template <> struct GT<f16> {
 // 32-row c tiles of one 32-token block.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ qn,
-                                                          const T* __restrict__ wuk,
-                                                          T* __restrict__ ql, int Tn, int H) {
+__device__ __forceinline__ void absorb_block(const T* __restrict__ qn, const T* __restrict__ wuk,
+                                             T* __restrict__ ql, int Tn, int H) {
   typedef typename GT<T>::v8 v8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = blockIdx.x;
@@ -99,6 +99,23 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ 
       }
     }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ qn,
+                                                          const T* __restrict__ wuk,
+                                                          T* __restrict__ ql, int Tn, int H) {
+  absorb_block<T>(qn, wuk, ql, Tn, H);
+}
+
+// The fused decode prologue: the absorption blocks (head, c half, token
+// block) also rotate head h's q_pe (c half 0) and, for head 0 / c half 1,
+// append the token block's cache rows.
+template <typename T>
+__global__ __launch_bounds__(256) void prologue_mfma_kernel(PrologueParams pp) {
+  absorb_block<T>((const T*)pp.q_nope, (const T*)pp.w_uk, (T*)pp.q_lat, pp.T, pp.H);
+  rope_append_block<T>(pp, blockIdx.x, blockIdx.z * 32, blockIdx.y == 0,
+                       blockIdx.x == 0 && blockIdx.y == 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -188,6 +205,15 @@ hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int Tn, i
   else
     hipLaunchKernelGGL(absorb_mfma_kernel<f16>, g, dim3(256), 0, st, (const f16*)qn,
                        (const f16*)w, (f16*)ql, Tn, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_prologue_mfma(const PrologueParams& pp, int dt, hipStream_t st) {
+  dim3 g(pp.H, kDc / 256, (pp.T + 31) / 32);
+  if (dt == MLA_BF16)
+    hipLaunchKernelGGL(prologue_mfma_kernel<bf16>, g, dim3(256), 0, st, pp);
+  else
+    hipLaunchKernelGGL(prologue_mfma_kernel<f16>, g, dim3(256), 0, st, pp);
   return hipGetLastError();
 }
 

@@ -5,6 +5,22 @@
 
 namespace mla {
 
+// arguments of the decode prologue (mla_prologue_args, validated)
+struct PrologueParams {
+  const void* q_nope;
+  const void* q_pe;
+  const void* w_uk;
+  const void* kv_new;
+  const int32_t* positions;
+  int B, S, H, T;
+  double log2_theta;
+  void* kv;
+  const int32_t* block_table;
+  int block_size, max_blocks, num_blocks, kv_seq_stride;
+  void* q_lat;
+  void* q_rope;
+};
+
 struct CombineParams {
   const void* parts_out;
   const void* parts_lse;
@@ -32,6 +48,10 @@ hipError_t launch_vup_mfma(const void* x, const void* w, void* out, int T, int H
                            hipStream_t st);
 hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int T, int H, int dt,
                               hipStream_t st);
+// fused absorption + rotation + cache append (bf16 / f16)
+hipError_t launch_prologue_mfma(const PrologueParams& pp, int dt, hipStream_t st);
+// rotation + cache append alone (any dtype; absorption launched separately)
+hipError_t launch_rope_append(const PrologueParams& pp, int dt, hipStream_t st);
 hipError_t launch_absorb_simple(const void* qn, const void* w, void* ql, int T, int H, int dt,
                                 hipStream_t st);
 

@@ -140,3 +140,37 @@ def test_valid_call_without_device_reports_hip_error():
                        timeout=300, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
     assert r.returncode == 0, r.stderr
     assert r.stdout.split() == ["-7", "-7"], r.stdout + r.stderr
+
+
+def prologue_base(**over):
+    a = L.PrologueArgs()
+    a.q_nope, a.q_pe, a.w_uk = FAKE, FAKE + 0x10000000, FAKE + 0x20000000
+    a.kv_new, a.positions = FAKE + 0x30000000, FAKE + 0x40000000
+    a.dtype = L.MLA_BF16
+    a.B, a.S, a.H = 2, 1, 128
+    a.rope_theta = 10000.0
+    a.kv, a.block_table = FAKE + 0x50000000, FAKE + 0x60000000
+    a.block_size, a.max_blocks, a.num_blocks = 32, 4, 8
+    a.q_lat, a.q_rope = FAKE + 0x70000000, FAKE + 0x80000000
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q_nope=None), -1), (dict(q_pe=None), -1), (dict(w_uk=None), -1),
+    (dict(kv_new=None), -1), (dict(positions=None), -1), (dict(kv=None), -1),
+    (dict(q_lat=None), -1), (dict(q_rope=None), -1), (dict(block_table=None), -1),
+    (dict(dtype=9), -3), (dict(B=0), -2), (dict(S=0), -2), (dict(H=0), -2),
+    (dict(max_blocks=0), -2), (dict(num_blocks=0), -2),
+    (dict(block_size=0), -2),  # contiguous layout takes no block table
+    (dict(block_size=0, block_table=None, kv_seq_stride=0), -2),
+    (dict(rope_theta=0.0), -4), (dict(rope_theta=float("nan")), -4),
+    (dict(rope_theta=float("inf")), -4),
+    (dict(q_lat=FAKE + 0x100), -8),           # q_lat overlaps q_nope
+    (dict(q_rope=FAKE + 0x50000000), -8),     # q_rope overlaps the cache
+    (dict(kv_new=FAKE + 0x50000040), -8),     # the new rows overlap the cache
+])
+def test_prologue_validation(over, code):
+    a = prologue_base(**over)
+    assert L.lib().mla_decode_prologue(ctypes.byref(a), None) == code
