@@ -248,9 +248,10 @@ struct Plan {
 };
 
 // Computes the plan; if `want` >= 0, also finds chunk `want`:
-// found = {unit, first tile, end tile, slot (-1 = direct), chunk index in unit}
+// found = {unit, first tile, end tile, slot (-1 = direct), chunk count of
+// the unit, split index, the unit's range}
 struct Found {
-  int u, tb, te, slot, nsplit, split_idx;
+  int u, tb, te, slot, nsplit, split_idx, st, en;
 };
 
 // units per thread whose ranges stay in registers through the plan
@@ -355,6 +356,8 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
         found->slot = n > 1 ? soff + k : -1;
         found->nsplit = n;
         found->split_idx = n > 1 ? poff : -1;
+        found->st = x.st;
+        found->en = x.en;
         break;
       }
       if (n > 1) {
@@ -414,24 +417,6 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned m
                : "memory");
 }
 
-// Normalised output of head 32 g + (lane & 31) over this wave's 128 latent
-// columns: lane (head, hi) holds columns 32 dt + 8 j + 4 hi + 0..3 in
-// o[4 dt + g][4 j + 0..3]; one 4-element vector store each.
-template <typename TO>
-__device__ __forceinline__ void store_rows(TO* dst, const floatx16* o, int g, int hi, float inv,
-                                           bool bad) {
-  typedef TO v4 __attribute__((ext_vector_type(4)));
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v4 v;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = from_f<TO>(bad ? NAN : o[4 * dt + g][4 * j + i] * inv);
-      *(v4*)(dst + dt * 32 + 8 * j + 4 * hi) = v;
-    }
-}
-
 template <typename T>
 __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
@@ -483,8 +468,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const int p = fd.u / pp.B, b = fd.u % pp.B;
   const int t = b * S + s;
   const int Tq = pp.B * S;
-  const int st = pp.range_start[fd.u];
-  const int en = pp.range_end[fd.u];
+  const int st = __builtin_amdgcn_readfirstlane(sh_found.st);
+  const int en = __builtin_amdgcn_readfirstlane(sh_found.en);
   const bool unit_bad = st < 0 || en < st || (long long)en > pp.capacity;
   int vend = en;
   if (pp.mask == MLA_MASK_CAUSAL_WINDOW) vend = min(en, en - S + s + 1);
@@ -547,11 +532,11 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       q[k] = d < kDc ? *(const v8*)(ql + d) : *(const v8*)(qr + (d - kDc));
     }
   }
-  // Complete the Q loads here: with nothing pending at loop entry the
-  // compiler places no vmcnt waits of its own inside the tile loop (it cannot
-  // see the LDS-direct loads, and a wait for an early Q load would otherwise
-  // drain every tile in flight).
-  wait_vm_all();
+  // The Q loads complete at the row table's wait (fill_rows), before the
+  // first tile load: with nothing pending at loop entry the compiler places
+  // no vmcnt waits of its own inside the tile loop (it cannot see the
+  // LDS-direct loads, and a wait for an early Q load would otherwise drain
+  // every tile in flight).
 
   floatx16 o[kDTiles];
 #pragma unroll
@@ -948,20 +933,54 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       pp.ws_lse[row0 + head] = lse;
   }
   __syncthreads();
+  // The normalised rows go out through the (now idle) stage buffers, 64
+  // heads at a time: each lane writes its values (head 32 g + r32, columns
+  // 128 wave + 32 dt + 8 j + 4 hi + 0..3, held in o[4 dt + g][4 j + 0..3])
+  // into a padded [64][512] block, then every store instruction writes 1 KB
+  // of one head's contiguous 512-value row.
+  auto store_out = [&](auto* dst) __attribute__((always_inline)) {
+    typedef std::remove_pointer_t<decltype(dst)> TO;
+    typedef TO v4 __attribute__((ext_vector_type(4)));
+    constexpr int kSz = (int)sizeof(TO);
+    constexpr int kPitch = kDc * kSz + 16;        // padded row: spreads the banks
+    constexpr int kRowPieces = kDc * kSz / 16;    // 16-byte pieces per row
+    static_assert(64 * kPitch <= kStages * kStageBytes, "output staging fits the stages");
 #pragma unroll
-  for (int g = 0; g < kWaves; ++g) {
-    const int h = g * kHeadsWave + r32;
-    const float ig = sh_inv[h];
-    const size_t e0 = (row0 + h) * kDc + kDc / kWaves * wave;
-    if (fd.slot >= 0)
-      store_rows<float>(pp.ws_out + e0, o, g, hi, ig, bad);
-    else if (pp.out_dtype == MLA_F32)
-      store_rows<float>((float*)pp.out + e0, o, g, hi, ig, bad);
-    else if (pp.out_dtype == MLA_BF16)
-      store_rows<bf16>((bf16*)pp.out + e0, o, g, hi, ig, bad);
-    else
-      store_rows<f16>((f16*)pp.out + e0, o, g, hi, ig, bad);
-  }
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int gg = 0; gg < 2; ++gg) {
+        const int g = 2 * half + gg;
+        const float ig = sh_inv[g * kHeadsWave + r32];
+        char* row = lds + (gg * kHeadsWave + r32) * kPitch;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v[i] = from_f<TO>(bad ? NAN : o[4 * dt + g][4 * j + i] * ig);
+            *(v4*)(row + (kDc / kWaves * wave + 32 * dt + 8 * j + 4 * hi) * kSz) = v;
+          }
+      }
+      __syncthreads();
+      char* out = (char*)(dst + (size_t)half * 64 * kDc);
+#pragma unroll
+      for (int idx = tid; idx < 64 * kRowPieces; idx += 256) {
+        const int r = idx / kRowPieces, c = idx % kRowPieces;
+        *(uint4*)(out + (size_t)r * kDc * kSz + c * 16) = *(const uint4*)(lds + r * kPitch + c * 16);
+      }
+      __syncthreads();
+    }
+  };
+  if (fd.slot >= 0)
+    store_out(pp.ws_out + row0 * kDc);
+  else if (pp.out_dtype == MLA_F32)
+    store_out((float*)pp.out + row0 * kDc);
+  else if (pp.out_dtype == MLA_BF16)
+    store_out((bf16*)pp.out + row0 * kDc);
+  else
+    store_out((f16*)pp.out + row0 * kDc);
 }
 
 // ---------------------------------------------------------------------------
