@@ -132,16 +132,6 @@ template <> struct MT<bf16> {
   static __device__ __forceinline__ void qk_next(floatx16& acc, v8 a, v8 b) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
   }
-  // starts two chains in one statement: the early-clobber outputs cannot
-  // alias any operand of either instruction
-  static __device__ __forceinline__ void qk_first2(floatx16& acc, floatx16& acc2, v8 a, v8 b,
-                                                   v8 a2, v8 b2) {
-    asm volatile(
-        "v_mfma_f32_32x32x16_bf16 %0, %2, %3, 0\n\t"
-        "v_mfma_f32_32x32x16_bf16 %1, %4, %5, 0"
-        : "=&v"(acc), "=&v"(acc2)
-        : "v"(a), "v"(b), "v"(a2), "v"(b2));
-  }
 };
 template <> struct MT<f16> {
   typedef f16x8 v8;
@@ -157,23 +147,13 @@ template <> struct MT<f16> {
   static __device__ __forceinline__ void qk_next(floatx16& acc, v8 a, v8 b) {
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
   }
-  // starts two chains in one statement: the early-clobber outputs cannot
-  // alias any operand of either instruction
-  static __device__ __forceinline__ void qk_first2(floatx16& acc, floatx16& acc2, v8 a, v8 b,
-                                                   v8 a2, v8 b2) {
-    asm volatile(
-        "v_mfma_f32_32x32x16_f16 %0, %2, %3, 0\n\t"
-        "v_mfma_f32_32x32x16_f16 %1, %4, %5, 0"
-        : "=&v"(acc), "=&v"(acc2)
-        : "v"(a), "v"(b), "v"(a2), "v"(b2));
-  }
 };
 
 // Wait states after the last score products before any other instruction
 // reads their results (more than the 8-pass result latency rule requires).
 // The accumulators are in/out operands, so no reader can be scheduled above.
-__device__ __forceinline__ void qk_drain(floatx16& a, floatx16& b) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a), "+v"(b)::"memory");
+__device__ __forceinline__ void qk_drain(floatx16& a) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(a)::"memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -759,56 +739,42 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     v8 wb0[kWaves], va01[2];
     const char* sb = lds + stage * kStageBytes;
 
-    // S^T = K . Q^T over 576 dims as two independent accumulation chains
-    // (k steps 0..17 and 18..35, issued alternately: a dependent matrix
-    // instruction would wait for its predecessor's result). Key operands
-    // rotate through a 6-entry ring, loaded 4 instructions ahead: a register
-    // is refilled only after the instruction two slots back has issued, so an
-    // LDS return can never overwrite an operand of a queued instruction (the
-    // compiler does not track these assembly instructions' operands).
-    constexpr int kHalf = kKSteps / 2;
-    constexpr int kRing = 6, kAhead = 4;
-    auto kstep = [](int n) { return (n & 1) ? kHalf + (n >> 1) : (n >> 1); };
+    // S^T = K . Q^T over 576 dims as one accumulation chain (a matrix
+    // instruction whose accumulator is its predecessor's result issues back
+    // to back). Key operands rotate through a kRing-entry ring, loaded kAhead
+    // instructions ahead: a register is refilled only after the instruction
+    // two slots back has issued, so an LDS return can never overwrite an
+    // operand of a queued instruction (the compiler does not track these
+    // assembly instructions' operands).
+    constexpr int kAhead = 8, kRing = kAhead + 2;
     auto kaddr = [&](int k) __attribute__((always_inline)) {
       return (const v8*)(sb + qk_off[k & 3] + (k >> 2) * 128);
     };
-    floatx16 sacc, sacc2;
+    floatx16 sacc;
     v8 kb[kRing];
 #pragma unroll
-    for (int n = 0; n < kAhead; ++n) kb[n] = *kaddr(kstep(n));
+    for (int n = 0; n < kAhead; ++n) kb[n] = *kaddr(n);
     // the carried group runs while the first key operands are in flight
     pv_group(3, cv, cw, 0, kWaves);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < kKSteps; ++n) {
-      const int k = kstep(n);
-      if (n == 0) {
-        // both chains start together (n = 0 and n = 1)
-        kb[kAhead % kRing] = *kaddr(kstep(kAhead));
-        MT<T>::qk_first2(sacc, sacc2, kb[0], q[0], kb[1], q[kHalf]);
-        kb[(kAhead + 1) % kRing] = *kaddr(kstep(kAhead + 1));
-        __builtin_amdgcn_sched_barrier(0);
-        continue;
-      }
-      if (n == 1) continue;
-      if (n & 1)
-        MT<T>::qk_next(sacc2, kb[n % kRing], q[k]);
+      if (n == 0)
+        MT<T>::qk_first(sacc, kb[0], q[0]);
       else
-        MT<T>::qk_next(sacc, kb[n % kRing], q[k]);
-      if (n + kAhead < kKSteps) kb[(n + kAhead) % kRing] = *kaddr(kstep(n + kAhead));
+        MT<T>::qk_next(sacc, kb[n % kRing], q[n]);
+      if (n + kAhead < kKSteps) kb[(n + kAhead) % kRing] = *kaddr(n + kAhead);
       if ((n & 3) == 2) issue_part(n >> 2);  // n = 2, 6, ..., 34: loads 0..8
-      // first operands of the value product, once the key ring stops loading
+      // first operands of the value product, in the last three slots
       // (harmless reads of stale data when there is no previous tile)
-      if (n == kKSteps - kAhead + 1)
+      if (n == kKSteps - 3)
 #pragma unroll
         for (int g = 0; g < kWaves; ++g) wb0[g] = wload(g, 0);
-      if (n == kKSteps - kAhead + 2) va01[0] = vload(pb, 0, 0);
-      if (n == kKSteps - kAhead + 3) va01[1] = vload(pb, 1, 0);
+      if (n == kKSteps - 2) va01[0] = vload(pb, 0, 0);
+      if (n == kKSteps - 1) va01[1] = vload(pb, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    qk_drain(sacc, sacc2);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] += sacc2[i];
+    qk_drain(sacc);
     // mask (only a range's last tile can be partial; exp2(-inf) = 0)
     const int tok0 = tile_tok0(j);
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
