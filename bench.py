@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -26,13 +27,23 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode µs/step, TFLOP/s & KV GB/s (% roofline) at B=32 H=128 L=32K"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
-KERNEL_SRC = os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", "partial_mfma.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", f)
+               for f in ("partial_mfma.hip", "common.h", "kernels.h")]
 PMC_FILE = os.path.join(ROOT, "profiles", "partial_mfma_kernel_pmc.json")
 
 
-def kernel_hash() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def kernel_hash(srcs=None) -> str:
+    """Hash of the partial kernel's code: its source and the headers it
+    includes, with // comments, blank lines and indentation dropped (a
+    comment edit does not invalidate counters taken on the same code)."""
+    h = hashlib.sha256()
+    for path in srcs or KERNEL_SRCS:
+        with open(path) as f:
+            for line in f:
+                code = re.sub(r"//.*", "", line).strip()
+                if code:
+                    h.update(code.encode() + b"\n")
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(workload: str):

@@ -15,13 +15,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla_decode.so")
 ARCH = "gfx950"
 
-# Per-source extra flags. The partial-attention kernel keeps ~400 live
-# registers (Q^T, the fp32 output and operand buffers); selecting the VGPR
-# form of the matrix instructions lets the allocator place them without
-# scratch spills.
-EXTRA_FLAGS = {
-
-}
+# Per-source extra hipcc flags, by file name (none needed at present).
+EXTRA_FLAGS = {}
 
 
 def hipcc() -> str:

@@ -11,7 +11,8 @@
 // Data flow per 32-token tile (one LDS stage of 32 x 576 x 2 B = 36 KB):
 //   HBM --buffer_load_dwordx4 ... lds--> LDS ring (4 stages, no VGPRs used)
 //   LDS --ds_read_b128--> key operand of S^T = K Q^T (32x32x16 MFMA, Q in VGPRs)
-//   online softmax in registers (each lane holds 16 tokens of one head)
+//   softmax in registers (each lane holds 16 tokens of one head; fixed
+//   exponent reference, below) --> weights P to an LDS buffer
 //   LDS --ds_read_b64_tr_b16--> transposed value operand of O^T += C^T P^T
 // LDS layout of a stage is row-major, 1152 bytes per key row, with the 16-byte
 // chunks of row r permuted within each 128-byte group: chunk c sits at
@@ -35,6 +36,15 @@
 // scores) is replayed once with each head's exact maximum as the reference.
 // The hot loop therefore never touches the output accumulators outside the
 // matrix instructions and needs no cross-lane maximum per tile.
+//
+// Step j of the tile loop: wait for tile j's loads and barrier; the score
+// product of tile j (one accumulation chain, key operands read 8 instructions
+// ahead), behind the value-product group carried over from the previous step;
+// the value product of tile j - 1 with tile j's softmax interleaved; barrier;
+// tile j's weights go to LDS between the instructions of one more value
+// group, and the last group is carried across the next barrier so the matrix
+// unit has work while the first key operands load. The loads of tile j + 2
+// are spread over the score product.
 //
 // Ranges that need splitting (few sequences, long ranges) are cut into
 // chunks; chunk results go to a fp32 workspace and a second kernel merges
