@@ -111,7 +111,9 @@ enum {
  * Workspace: `workspace_bytes` >= mla_decode_partial_workspace_size(args)
  *   bytes of device memory (may be 0 bytes / NULL when the size is 0). It is
  *   exclusive to the call until the stream has passed it; two calls that
- *   share a workspace must be ordered on one stream (or by events).
+ *   share a workspace must be ordered on one stream (or by events). It holds
+ *   the results of sub-ranges (in out_dtype, with fp32 LSEs) until they are
+ *   merged inside the call.
  * num_splits: 0 = automatic; otherwise each (part, sequence) range is cut
  *   into at most this many sub-ranges that are merged inside the call.
  */

@@ -44,7 +44,7 @@ bool use_mfma(const mla_partial_args* a) {
 
 size_t partial_ws_bytes(const mla_partial_args* a) {
   if (!use_mfma(a)) return 0;
-  return mfma_workspace_bytes(a->B, a->S, a->H, a->P, a->num_splits);
+  return mfma_workspace_bytes(a->B, a->S, a->H, a->P, a->num_splits, a->out_dtype);
 }
 
 // Validation without the workspace check; returns MLA_OK or an error code.
@@ -155,7 +155,7 @@ int mla_decode_partial(const mla_partial_args* a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (use_mfma(a)) {
-    pp.ws_out = (float*)a->workspace;  // workspace base; the launcher lays it out
+    pp.ws_out = a->workspace;  // workspace base; the launcher lays it out
     pp.max_chunks = (int)mfma_max_chunks(a->B, a->S, a->P, a->num_splits);
     e = launch_partial_mfma(pp, a->q_dtype, s);
   } else {

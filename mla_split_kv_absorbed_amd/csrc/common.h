@@ -71,7 +71,7 @@ struct PartialParams {
   const int32_t* range_end;
   void* out;
   void* lse;
-  float* ws_out;    // split partials [slot][S][H][512] fp32
+  void* ws_out;     // split partials [slot][S][H][512] in out_dtype
   float* ws_lse;    // split partials [slot][S][H] fp32
   int B, S, H, P;
   int block_size, max_blocks, num_blocks, kv_seq_stride;

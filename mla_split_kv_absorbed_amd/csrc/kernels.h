@@ -39,7 +39,7 @@ hipError_t launch_partial_mfma(const PartialParams& pp, int dtype, hipStream_t s
 // Upper bound on split sub-ranges ("slots") an MFMA-path call may write.
 size_t mfma_max_slots(int B, int S, int P, int num_splits);
 size_t mfma_max_chunks(int B, int S, int P, int num_splits);
-size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits);
+size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits, int out_dtype);
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t st);
 hipError_t launch_vup_simple(const void* x, const void* w, void* out, int T, int H, int dt,

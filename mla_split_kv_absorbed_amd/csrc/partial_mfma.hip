@@ -359,7 +359,8 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
   return pl;
 }
 
-// workspace layout: [count | pad 256][split descriptors U x int4][lse][out]
+// workspace layout: [count | pad 256][split descriptors U x int4][lse fp32][out,
+// in the output type]
 struct WsLayout {
   size_t desc_off, lse_off, out_off, total;
 };
@@ -373,14 +374,14 @@ __host__ __device__ inline size_t slots_bound(int B, int S, int P, int hint) {
   return (2 * kTargetGroups + S - 1) / S + 1;
 }
 
-__host__ __device__ inline WsLayout ws_layout(int B, int S, int H, int P, int hint) {
+__host__ __device__ inline WsLayout ws_layout(int B, int S, int H, int P, int hint, int out_dtype) {
   WsLayout w;
   const size_t U = (size_t)P * B;
   const size_t rows = slots_bound(B, S, P, hint) * S * H;
   w.desc_off = 256;
   w.lse_off = align256(w.desc_off + U * 16);
   w.out_off = align256(w.lse_off + rows * 4);
-  w.total = align256(w.out_off + rows * kDc * 4);
+  w.total = align256(w.out_off + rows * kDc * (out_dtype == MLA_F32 ? 4 : 2));
   return w;
 }
 
@@ -949,14 +950,14 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       __syncthreads();
     }
   };
-  if (fd.slot >= 0)
-    store_out(pp.ws_out + row0 * kDc);
-  else if (pp.out_dtype == MLA_F32)
-    store_out((float*)pp.out + row0 * kDc);
+  // a chunk of a cut range goes to the workspace, in the output type
+  void* dst = fd.slot >= 0 ? pp.ws_out : pp.out;
+  if (pp.out_dtype == MLA_F32)
+    store_out((float*)dst + row0 * kDc);
   else if (pp.out_dtype == MLA_BF16)
-    store_out((bf16*)pp.out + row0 * kDc);
+    store_out((bf16*)dst + row0 * kDc);
   else
-    store_out((f16*)pp.out + row0 * kDc);
+    store_out((f16*)dst + row0 * kDc);
 }
 
 // ---------------------------------------------------------------------------
@@ -972,8 +973,18 @@ __device__ __forceinline__ void store8(TO* dst, const float* v) {
   *(v8o*)dst = x;
 }
 
-// Lane i holds the LSE of chunk i0 + i; the chunks' partial rows are then
-// accumulated in ascending order, 4 rows in flight.
+// 8 consecutive values of a partial row stored in the output type
+template <typename TO>
+__device__ __forceinline__ void load8(const TO* src, float* v) {
+  typedef TO v8o __attribute__((ext_vector_type(8)));
+  const v8o x = *(const v8o*)src;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
+}
+
+// Lane i holds the LSE of chunk i0 + i; the chunks' partial rows (in the
+// output type TO) are then accumulated in ascending order, 4 rows in flight.
+template <typename TO>
 __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
   const int lane = threadIdx.x & 63;
@@ -1006,28 +1017,17 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
         const float wl = li == -INFINITY ? 0.f : expf(li - m);
         z += wave_sum(wl);
         for (int i = 0; i < cnt; i += 4) {
-          float4 a[4], c[4];
+          float a[4][8];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (i + q < cnt) {
-              const float4* src = (const float4*)(pp.ws_out + wrow(i0 + i + q) * kDc + lane * 8);
-              a[q] = src[0];
-              c[q] = src[1];
-            }
-          }
+          for (int q = 0; q < 4; ++q)
+            if (i + q < cnt)
+              load8<TO>((const TO*)pp.ws_out + wrow(i0 + i + q) * kDc + lane * 8, a[q]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float w = __shfl(wl, i + q, 64);
-            if (i + q < cnt && w != 0.f) {
-              acc[0] = fmaf(w, a[q].x, acc[0]);
-              acc[1] = fmaf(w, a[q].y, acc[1]);
-              acc[2] = fmaf(w, a[q].z, acc[2]);
-              acc[3] = fmaf(w, a[q].w, acc[3]);
-              acc[4] = fmaf(w, c[q].x, acc[4]);
-              acc[5] = fmaf(w, c[q].y, acc[5]);
-              acc[6] = fmaf(w, c[q].z, acc[6]);
-              acc[7] = fmaf(w, c[q].w, acc[7]);
-            }
+            if (i + q < cnt && w != 0.f)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, a[q][e], acc[e]);
           }
         }
       }
@@ -1046,13 +1046,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
       for (int i = 0; i < 8; ++i) acc[i] = 0.f;
       lse = -INFINITY;
     }
-    const size_t e0 = orow * kDc + lane * 8;
-    if (pp.out_dtype == MLA_F32)
-      store8<float>((float*)pp.out + e0, acc);
-    else if (pp.out_dtype == MLA_BF16)
-      store8<bf16>((bf16*)pp.out + e0, acc);
-    else
-      store8<f16>((f16*)pp.out + e0, acc);
+    store8<TO>((TO*)pp.out + orow * kDc + lane * 8, acc);
     if (lane == 0) store_any(pp.lse, orow, pp.lse_dtype, lse);
   }
 }
@@ -1074,19 +1068,19 @@ size_t mfma_max_chunks(int B, int S, int P, int hint) {
   return U + (kTargetGroups + S - 1) / S + 1;
 }
 
-size_t mfma_workspace_bytes(int B, int S, int H, int P, int hint) {
-  return ws_layout(B, S, H, P, hint).total;
+size_t mfma_workspace_bytes(int B, int S, int H, int P, int hint, int out_dtype) {
+  return ws_layout(B, S, H, P, hint, out_dtype).total;
 }
 
 hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_t st) {
   MfmaParams mp;
   mp.pp = pp_in;
-  const WsLayout w = ws_layout(pp_in.B, pp_in.S, pp_in.H, pp_in.P, pp_in.num_splits);
+  const WsLayout w = ws_layout(pp_in.B, pp_in.S, pp_in.H, pp_in.P, pp_in.num_splits, pp_in.out_dtype);
   char* ws = (char*)pp_in.ws_out;  // base of the workspace
   mp.ws_count = (int*)ws;
   mp.ws_desc = (intx4*)(ws + w.desc_off);
   mp.pp.ws_lse = (float*)(ws + w.lse_off);
-  mp.pp.ws_out = (float*)(ws + w.out_off);
+  mp.pp.ws_out = ws + w.out_off;
   const size_t chunks = mfma_max_chunks(pp_in.B, pp_in.S, pp_in.P, pp_in.num_splits);
   size_t groups = chunks * pp_in.S;
   if (pp_in.S > 1) groups = (groups + 8 * pp_in.S - 1) / (8 * pp_in.S) * (8 * pp_in.S);
@@ -1107,7 +1101,12 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
   const size_t merge_rows = split_units * pp_in.S * pp_in.H;
   const unsigned merge_blocks = (unsigned)std::max<size_t>(
       1, std::min<size_t>((merge_rows + 3) / 4, 2048));
-  hipLaunchKernelGGL(split_merge_kernel, dim3(merge_blocks), dim3(256), 0, st, mp);
+  if (pp_in.out_dtype == MLA_F32)
+    hipLaunchKernelGGL(split_merge_kernel<float>, dim3(merge_blocks), dim3(256), 0, st, mp);
+  else if (pp_in.out_dtype == MLA_BF16)
+    hipLaunchKernelGGL(split_merge_kernel<bf16>, dim3(merge_blocks), dim3(256), 0, st, mp);
+  else
+    hipLaunchKernelGGL(split_merge_kernel<f16>, dim3(merge_blocks), dim3(256), 0, st, mp);
   return hipGetLastError();
 }
 
