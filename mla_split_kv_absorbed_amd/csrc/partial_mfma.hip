@@ -685,10 +685,11 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
 #pragma unroll
       for (int g = 0; g < kWaves; ++g) {
         o[dt * 4 + g] = MT<T>::mfma(va[n & 3], wb[kk][g], o[dt * 4 + g]);
-        // the 16 weights spread over the 24 instructions
+        // the 16 weights spread over instructions 4..23 (4 of every 5
+        // slots): the first 4 cover the score product's result latency
         if constexpr (kSoft) {
-          const int m = 4 * n + g;
-          if (m % 3 != 2) weight(m - m / 3);
+          const int m = 4 * n + g - 4;
+          if (m >= 0 && m % 5 != 4) weight(m - m / 5);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -785,11 +786,14 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       if (n == kKSteps - 1) va01[1] = vload(pb, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
-    qk_drain(sacc);
+    // The scores are read by vector instructions only after the result
+    // latency of the last score product: behind qk_drain(), or, in the value
+    // product, behind its first 4 matrix instructions (>= 128 cycles).
     // mask (only a range's last tile can be partial; exp2(-inf) = 0)
     const int tok0 = tile_tok0(j);
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
     if (nvis < kTile) {
+      qk_drain(sacc);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 8 * (i >> 2) + 4 * hi + (i & 3);
@@ -804,6 +808,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       pv(pb, std::integral_constant<bool, true>(), sacc, pk, wb0, va01, cw, va67);
     } else {
       // first tile of a segment: the weights alone (same arithmetic)
+      qk_drain(sacc);
       float pf_even = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
