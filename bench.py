@@ -4,8 +4,8 @@ Default workload: B=32, H=128, q_len=1, L=32768 per sequence, paged latent
 cache (block 32, blocks in a seeded random permutation), keys split into 8
 contiguous parts of 4096 (decode context parallelism emulated on one GPU),
 bf16 partial outputs and LSEs, LSE combine, V-up. One step = q-absorb +
-partial attention over all parts + LSE combine + V-up, inputs resident in
-HBM. Prints one JSON line.
+partial attention over all parts + LSE combine + V-up (the last two as one
+fused launch for bf16 / fp16), inputs resident in HBM. Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2]
 """
@@ -177,14 +177,19 @@ def main():
         ev[i][1].record(stream)
         if sp.current:
             L.mla_decode_partial(st.cur_args, stream)
-        if st.skip_combine:
-            x = st.parts_out[0]
-        else:
-            L.mla_lse_combine(st.parts_out, st.parts_lse, st.lat, st.lse,
+        if st.fused_tail:
+            L.mla_combine_vup(st.parts_out, st.parts_lse, st.w_uv, st.out, st.lse,
                               local_out=st.cur_out if sp.current else None,
                               local_lse=st.cur_lse if sp.current else None, stream=stream)
-            x = st.lat
-        L.mla_vup(x, st.w_uv, st.out, stream)
+        else:
+            if st.skip_combine:
+                x = st.parts_out[0]
+            else:
+                L.mla_lse_combine(st.parts_out, st.parts_lse, st.lat, st.lse,
+                                  local_out=st.cur_out if sp.current else None,
+                                  local_lse=st.cur_lse if sp.current else None, stream=stream)
+                x = st.lat
+            L.mla_vup(x, st.w_uv, st.out, stream)
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0

@@ -175,6 +175,23 @@ int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int par
                     int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
                     void* out, int out_dtype, float* lse_out, void* stream);
 
+/* LSE combine fused with V-up: the result of mla_lse_combine followed by
+ * mla_vup in one launch, the merged latent kept on chip (study page: the
+ * combine step feeds the batch-major latent straight into the fused V-up).
+ *   parts_out / parts_lse / P / part_dtype / lse_dtype / local_out /
+ *   local_lse / T / H: as in mla_lse_combine.
+ *   dtype: MLA_BF16 or MLA_F16 (MLA_ERR_UNSUPPORTED for MLA_F32: call the
+ *   two entry points). The merged latent is rounded to `dtype` before the
+ *   product, exactly as mla_lse_combine would store it for mla_vup.
+ *   w_uv [H][512][128] (dtype); out [T][H][128] (dtype) == [T][H*128];
+ *   lse_out fp32 [T][H] or NULL; lat_out [T][H][512] (dtype) or NULL: the
+ *   merged latent as mla_lse_combine writes it.
+ * Outputs must not overlap the inputs or each other (MLA_ERR_ALIAS). */
+int mla_combine_vup(const void* parts_out, const void* parts_lse, int P, int part_dtype,
+                    int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
+                    const void* w_uv, int dtype, void* out, float* lse_out, void* lat_out,
+                    void* stream);
+
 /* V-up on the batch-major latent, transpose-free (study page, V-up fusion):
  *   out[t][h][v] = sum_c x[t][h][c] * W_UV[h][c][v]
  *   x [T][H][512], w_uv [H][512][128], out [T][H][128] == [T][H*128]. */

@@ -92,6 +92,9 @@ def lib():
         L.mla_vup.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         L.mla_lse_combine.restype = ci
         L.mla_lse_combine.argtypes = [vp, vp, ci, ci, ci, vp, vp, ci, ci, vp, ci, vp, vp]
+        L.mla_combine_vup.restype = ci
+        L.mla_combine_vup.argtypes = [vp, vp, ci, ci, ci, vp, vp, ci, ci, vp, ci, vp, vp, vp,
+                                      vp]
         L.mla_decode_prologue.restype = ci
         L.mla_decode_prologue.argtypes = [ctypes.POINTER(PrologueArgs), vp]
         _lib = L
@@ -185,6 +188,21 @@ def mla_lse_combine(parts_out, parts_lse, out, lse_out=None, local_out=None, loc
                                  DT_CODE[refl.dtype], _ptr(local_out), _ptr(local_lse), T, H,
                                  _ptr(out), DT_CODE[out.dtype], _ptr(lse_out), _stream(stream)),
            "mla_lse_combine")
+
+
+def mla_combine_vup(parts_out, parts_lse, w_uv, out, lse_out=None, lat_out=None,
+                    local_out=None, local_lse=None, stream=None):
+    """parts_out [P][T][H][512] (P may be 0 / None with a local part),
+    w_uv [H][512][128], out [T][H][128] in the compute dtype."""
+    ref = parts_out if parts_out is not None else local_out
+    refl = parts_lse if parts_lse is not None else local_lse
+    P = parts_out.shape[0] if parts_out is not None else 0
+    T, H = out.shape[0], out.shape[1]
+    _check(lib().mla_combine_vup(_ptr(parts_out), _ptr(parts_lse), P, DT_CODE[ref.dtype],
+                                 DT_CODE[refl.dtype], _ptr(local_out), _ptr(local_lse), T, H,
+                                 _ptr(w_uv), DT_CODE[out.dtype], _ptr(out), _ptr(lse_out),
+                                 _ptr(lat_out), _stream(stream)),
+           "mla_combine_vup")
 
 
 def prologue_args(q_nope, q_pe, w_uk, kv_new, positions, kv, q_lat, q_rope, *, B, S,

@@ -200,6 +200,54 @@ int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int par
   return launch_combine(c, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_combine_vup(const void* parts_out, const void* parts_lse, int P, int part_dtype,
+                    int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
+                    const void* w_uv, int dtype, void* out, float* lse_out, void* lat_out,
+                    void* stream) {
+  if (!out || !w_uv) return MLA_ERR_NULL;
+  if ((local_out == nullptr) != (local_lse == nullptr)) return MLA_ERR_NULL;
+  if (P > 0 && (!parts_out || !parts_lse)) return MLA_ERR_NULL;
+  if (!valid_dtype(part_dtype) || !valid_dtype(lse_dtype) || !valid_dtype(dtype))
+    return MLA_ERR_DTYPE;
+  if (P < 0 || T < 1 || H < 1 || H > 65535) return MLA_ERR_SHAPE;
+  if (P + (local_out ? 1 : 0) < 1) return MLA_ERR_SHAPE;
+  if (dtype == MLA_F32) return MLA_ERR_UNSUPPORTED;
+  // tokens per workgroup: 16 when that makes at most 256 workgroups (about
+  // one per CU: small batches still spread over the chip), else 32 (each
+  // workgroup re-reads W_UV[h], so fewer, larger blocks beyond that)
+  const int tb = (size_t)H * ((T + 15) / 16) <= 256 ? 16 : 32;
+  if ((T + tb - 1) / tb > 65535) return MLA_ERR_SHAPE;
+  const size_t rows = (size_t)T * H;
+  const size_t pe = elem_bytes(part_dtype), le = elem_bytes(lse_dtype), e = elem_bytes(dtype);
+  Extent ins[5] = {{parts_out, (size_t)P * rows * kDc * pe},
+                   {parts_lse, (size_t)P * rows * le},
+                   {local_out, local_out ? rows * kDc * pe : 0},
+                   {local_lse, local_lse ? rows * le : 0},
+                   {w_uv, (size_t)H * kDc * kDv * e}};
+  Extent outs[3] = {{out, rows * kDv * e},
+                    {lse_out, lse_out ? rows * 4 : 0},
+                    {lat_out, lat_out ? rows * kDc * e : 0}};
+  if (any_overlap(outs, 3, ins, 5)) return MLA_ERR_ALIAS;
+  CombineVupParams cv;
+  cv.c.parts_out = parts_out;
+  cv.c.parts_lse = parts_lse;
+  cv.c.local_out = local_out;
+  cv.c.local_lse = local_lse;
+  cv.c.out = nullptr;
+  cv.c.lse_out = lse_out;
+  cv.c.P = P;
+  cv.c.T = T;
+  cv.c.H = H;
+  cv.c.part_dtype = part_dtype;
+  cv.c.lse_dtype = lse_dtype;
+  cv.c.out_dtype = dtype;
+  cv.w_uv = w_uv;
+  cv.out = out;
+  cv.lat_out = lat_out;
+  cv.tb = tb;
+  return launch_combine_vup(cv, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
 int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype, void* stream) {
   if (!x || !w_uv || !out) return MLA_ERR_NULL;
   if (!valid_dtype(dtype)) return MLA_ERR_DTYPE;

@@ -40,12 +40,11 @@ __device__ __forceinline__ float part_lse(const CombineParams& c, int i, size_t 
                  : load_any(c.local_lse, row, c.lse_dtype);
 }
 
-template <typename TP, typename TO>
-__global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
-  const int lane = threadIdx.x & 63;
-  const size_t rows = (size_t)c.T * c.H;
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+// Merge of one (token, head) row by one wave: lane l returns the merged
+// values 8 l .. 8 l + 7 in o[] and the row's LSE.
+template <typename TP>
+__device__ __forceinline__ float merge_row(const CombineParams& c, size_t row, size_t rows,
+                                           int lane, float* o) {
   const int np = c.P + (c.local_out ? 1 : 0);
 
   // lane i holds the LSE of part i0 + i: the maximum and the weights take
@@ -91,7 +90,6 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
       }
     }
   }
-  float o[8];
   float lse;
   if (nan_seen) {
 #pragma unroll
@@ -107,6 +105,17 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
     for (int k = 0; k < 8; ++k) o[k] = 0.f;
     lse = -INFINITY;
   }
+  return lse;
+}
+
+template <typename TP, typename TO>
+__global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
+  const int lane = threadIdx.x & 63;
+  const size_t rows = (size_t)c.T * c.H;
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  float o[8];
+  const float lse = merge_row<TP>(c, row, rows, lane, o);
   store8<TO>((TO*)c.out + row * kDc + lane * 8, o);
   if (c.lse_out && lane == 0) c.lse_out[row] = lse;
 }
@@ -127,6 +136,145 @@ hipError_t launch_combine(const CombineParams& c, hipStream_t st) {
   if (c.part_dtype == MLA_F32) launch_combine_out<float>(c, g, st);
   else if (c.part_dtype == MLA_BF16) launch_combine_out<bf16>(c, g, st);
   else launch_combine_out<f16>(c, g, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// LSE combine fused with V-up. One workgroup per (head h, block of tb <= 32
+// tokens): its 4 waves merge the block's latent rows of head h (one row per
+// wave at a time, as combine_kernel), round them to the compute type into
+// LDS, then run out^T[v][t] = sum_c W_UV[h][c][v] x[t][c] on the matrix
+// cores in two 64-column passes; W_UV[h] is loaded into registers before the
+// merge, so its memory round trip overlaps the part reads. The merged latent
+// never goes to HBM (unless lat_out asks for it).
+// ---------------------------------------------------------------------------
+#define LDS_AS __attribute__((address_space(3)))
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+template <typename T> struct CvT;
+template <> struct CvT<bf16> {
+  typedef __bf16 v8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct CvT<f16> {
+  typedef _Float16 v8 __attribute__((ext_vector_type(8)));
+  typedef _Float16 v4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+};
+
+constexpr int kCvCols = 64;                           // W_UV columns per pass
+constexpr int kCvWRow = kCvCols * 2 + 32;             // LDS bytes per W row (padded)
+constexpr int kCvXRow = kDc * 2 + 16;                 // LDS bytes per latent row (padded)
+constexpr int kCvWaves = 16;                         // rows merged concurrently
+constexpr int kCvThreads = kCvWaves * 64;
+constexpr int kCvPieces = kDc * kCvCols * 2 / 16 / kCvThreads;  // 16-byte W pieces per thread per pass
+static_assert(kCvPieces * kCvThreads * 16 == kDc * kCvCols * 2, "W pass split");
+
+template <typename TP, typename T>
+__global__ __launch_bounds__(kCvThreads) void combine_vup_kernel(CombineVupParams cv) {
+  typedef typename CvT<T>::v8 v8;
+  __shared__ __attribute__((aligned(16))) char wl[kDc * kCvWRow];
+  __shared__ __attribute__((aligned(16))) char xl[32 * kCvXRow];
+  const CombineParams& c = cv.c;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x;
+  const int t0 = blockIdx.y * cv.tb;
+  const int nt = min(cv.tb, c.T - t0);
+  const size_t rows = (size_t)c.T * c.H;
+
+  // W_UV[h][:, 64 p .. 64 p + 63] for both passes p: 512 rows x 128 B each
+  const T* wsrc = (const T*)cv.w_uv + (size_t)h * kDc * kDv;
+  v8 st[2][kCvPieces];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int i = 0; i < kCvPieces; ++i) {
+      const int idx = tid + i * kCvThreads, cc = idx >> 3, q = idx & 7;
+      st[p][i] = *(const v8*)(wsrc + (size_t)cc * kDv + p * kCvCols + q * 8);
+    }
+
+  // merged latent rows of the block, rounded to T as a stored latent would be
+  for (int r = wave; r < 32; r += kCvWaves) {
+    v8 xv;
+    if (r < nt) {
+      const size_t row = (size_t)(t0 + r) * c.H + h;
+      float o[8];
+      const float lse = merge_row<TP>(c, row, rows, lane, o);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = from_f<T>(o[e]);
+      if (cv.lat_out) *(v8*)((T*)cv.lat_out + row * kDc + lane * 8) = xv;
+      if (c.lse_out && lane == 0) c.lse_out[row] = lse;
+    } else {
+      // columns past the block: their products are never stored
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[e] = (T)0.f;
+    }
+    *(v8*)(xl + r * kCvXRow + lane * 16) = xv;
+  }
+
+  const int r32 = lane & 31, hi = lane >> 5;
+  const int j16 = lane & 15, g16 = lane >> 4;
+  // A = W^T (rows v, k = c) by transposed reads: 16-lane block g16 covers
+  // v 16 (g16 & 1) .. + 15 and c rows 8 (g16 >> 1) .. of each 16-wide k step
+  const int a_off = ((8 * (g16 >> 1) + (j16 >> 2)) * kCvWRow) +
+                    ((wave & 1) * 32 + 16 * (g16 & 1) + 4 * (j16 & 3)) * 2;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    if (p) __syncthreads();  // every wave is done reading the previous pass
+#pragma unroll
+    for (int i = 0; i < kCvPieces; ++i) {
+      const int idx = tid + i * kCvThreads, cc = idx >> 3, q = idx & 7;
+      *(v8*)(wl + cc * kCvWRow + q * 16) = st[p][i];
+    }
+    __syncthreads();
+    // waves 0 and 1 take the pass's two 32-column tiles, B = x^T column t
+    if (wave < 2) {
+      floatx16 acc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int k = 0; k < kDc / 16; ++k) {
+        const char* a0 = wl + a_off + k * 16 * kCvWRow;
+        const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)a0);
+        const shortx4 h4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(a0 + 4 * kCvWRow));
+        const v8 a = __builtin_bit_cast(v8, __builtin_shufflevector(lo, h4, 0, 1, 2, 3, 4, 5, 6, 7));
+        const v8 b = *(const v8*)(xl + r32 * kCvXRow + (16 * k + 8 * hi) * 2);
+        acc = CvT<T>::mfma(a, b, acc);
+      }
+      if (r32 < nt) {
+        T* dst = (T*)cv.out + ((size_t)(t0 + r32) * c.H + h) * kDv + p * kCvCols + wave * 32 + 4 * hi;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typename CvT<T>::v4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = from_f<T>(acc[4 * g + i]);
+          *(typename CvT<T>::v4*)(dst + 8 * g) = v;
+        }
+      }
+    }
+  }
+}
+
+template <typename TP>
+static void launch_combine_vup_t(const CombineVupParams& cv, dim3 g, hipStream_t st) {
+  if (cv.c.out_dtype == MLA_BF16)
+    hipLaunchKernelGGL((combine_vup_kernel<TP, bf16>), g, dim3(kCvThreads), 0, st, cv);
+  else
+    hipLaunchKernelGGL((combine_vup_kernel<TP, f16>), g, dim3(kCvThreads), 0, st, cv);
+}
+
+hipError_t launch_combine_vup(const CombineVupParams& cv, hipStream_t st) {
+  dim3 g((unsigned)cv.c.H, (unsigned)((cv.c.T + cv.tb - 1) / cv.tb));
+  if (cv.c.part_dtype == MLA_F32) launch_combine_vup_t<float>(cv, g, st);
+  else if (cv.c.part_dtype == MLA_BF16) launch_combine_vup_t<bf16>(cv, g, st);
+  else launch_combine_vup_t<f16>(cv, g, st);
   return hipGetLastError();
 }
 

@@ -42,6 +42,17 @@ size_t mfma_max_chunks(int B, int S, int P, int num_splits);
 size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits, int out_dtype);
 
 hipError_t launch_combine(const CombineParams& c, hipStream_t st);
+
+// combine fused with V-up: c.out_dtype is the compute type (bf16 / f16) of
+// w_uv, out and lat_out; tokens per workgroup tb in [1, 32]
+struct CombineVupParams {
+  CombineParams c;
+  const void* w_uv;
+  void* out;      // [T][H][128]
+  void* lat_out;  // [T][H][512] or NULL
+  int tb;
+};
+hipError_t launch_combine_vup(const CombineVupParams& cv, hipStream_t st);
 hipError_t launch_vup_simple(const void* x, const void* w, void* out, int T, int H, int dt,
                              hipStream_t st);
 hipError_t launch_vup_mfma(const void* x, const void* w, void* out, int T, int H, int dt,

@@ -47,7 +47,7 @@ class DecodeStep:
 
     def __init__(self, w: Workload, device="cuda", part_lse_dtype: Optional[str] = None,
                  num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None,
-                 side_stream: bool = False):
+                 side_stream: bool = False, fused_tail: bool = True, keep_latent: bool = False):
         sp = w.spec
         self.w = w
         self.dev = torch.device(device)
@@ -125,6 +125,11 @@ class DecodeStep:
         # merged latent; the combine is skipped
         self.skip_combine = (P == 1 and not sp.current and pdt == odt
                              and self.parts_lse.dtype == torch.float32)
+        # combine and V-up as one launch (bf16 / fp16); the merged latent is
+        # then written only with keep_latent
+        self.fused_tail = (fused_tail and not self.skip_combine and odt == self.dt
+                           and dt in ("bf16", "f16"))
+        self.keep_latent = keep_latent or not self.fused_tail
 
     def run(self, stream=None):
         main = stream if stream is not None else torch.cuda.current_stream(self.dev)
@@ -143,6 +148,13 @@ class DecodeStep:
             if self.w.spec.current:
                 L.mla_decode_partial(self.cur_args, main)
         stream = main
+        if self.fused_tail:
+            L.mla_combine_vup(self.parts_out, self.parts_lse, self.w_uv, self.out, self.lse,
+                              lat_out=self.lat if self.keep_latent else None,
+                              local_out=self.cur_out if self.w.spec.current else None,
+                              local_lse=self.cur_lse if self.w.spec.current else None,
+                              stream=stream)
+            return self.out
         if self.skip_combine:
             x = self.parts_out[0]
         else:
@@ -158,4 +170,7 @@ class DecodeStep:
         return self.parts_lse[0] if self.skip_combine else self.lse
 
     def final_latent(self) -> torch.Tensor:
+        if not self.keep_latent:
+            raise RuntimeError("the fused combine + V-up did not write the merged latent "
+                               "(construct with keep_latent=True)")
         return self.parts_out[0] if self.skip_combine else self.lat

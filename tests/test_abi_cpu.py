@@ -122,6 +122,34 @@ def test_combine_vup_absorb_validation():
     assert lib.mla_q_absorb(FAKE, FAKE * 64, FAKE + 100, 4, 8, 1, None) == -8
 
 
+def test_fused_combine_vup_validation():
+    cv = L.lib().mla_combine_vup
+    # parts [2][4][8][512] bf16 at FAKE, LSEs at 4 FAKE, W_UV [8][512][128] at
+    # 64 FAKE, out [4][8][128] at 128 FAKE, lat_out at 256 FAKE, lse_out at 512 FAKE
+    P, W, O, X, LS = FAKE * 4, FAKE * 64, FAKE * 128, FAKE * 256, FAKE * 512
+
+    def call(**over):
+        a = dict(parts=FAKE, lse=P, n=2, pdt=1, ldt=0, lo=None, ll=None, T=4, H=8, w=W, dt=1,
+                 out=O, lse_out=LS, lat=X)
+        a.update(over)
+        return cv(a["parts"], a["lse"], a["n"], a["pdt"], a["ldt"], a["lo"], a["ll"], a["T"],
+                  a["H"], a["w"], a["dt"], a["out"], a["lse_out"], a["lat"], None)
+    assert call(out=None) == -1
+    assert call(w=None) == -1
+    assert call(lo=FAKE * 1024) == -1          # local part without its LSE
+    assert call(parts=None) == -1
+    assert call(pdt=9) == -3
+    assert call(dt=7) == -3
+    assert call(T=0) == -2
+    assert call(H=0) == -2
+    assert call(n=0) == -2                     # no part at all
+    assert call(n=-1) == -2
+    assert call(dt=0) == -6                    # fp32: the two separate calls
+    assert call(out=FAKE + 64) == -8           # out overlaps the parts
+    assert call(lat=W + 4096) == -8            # merged latent overlaps W_UV
+    assert call(lse_out=O + 64) == -8          # the two outputs overlap
+
+
 NO_DEVICE = r"""
 import ctypes, math, sys
 sys.path.insert(0, %r)
@@ -129,6 +157,8 @@ from mla_split_kv_absorbed_amd import _lib as L
 from tests.test_abi_cpu import base_args
 print(L.lib().mla_decode_partial(ctypes.byref(base_args()), None))
 print(L.lib().mla_vup(0x10000, 0x20000000, 0x40000000, 4, 8, 1, None))
+print(L.lib().mla_combine_vup(0x10000, 0x400000, 2, 1, 0, None, None, 4, 8, 0x1000000, 1,
+                              0x4000000, None, None, None))
 """
 
 
@@ -139,7 +169,7 @@ def test_valid_call_without_device_reports_hip_error():
     r = subprocess.run([sys.executable, "-c", NO_DEVICE % ROOT], capture_output=True, text=True,
                        timeout=300, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
     assert r.returncode == 0, r.stderr
-    assert r.stdout.split() == ["-7", "-7"], r.stdout + r.stderr
+    assert r.stdout.split() == ["-7", "-7", "-7"], r.stdout + r.stderr
 
 
 def prologue_base(**over):

@@ -375,6 +375,62 @@ def test_combine(pdt, ldt, local):
     assert np.abs(gl[fin] - ref_l[fin]).max() <= 2e-5 * max(1.0, np.abs(ref_l[fin]).max())
 
 
+@pytest.mark.parametrize("pdt,ldt,dt,n,local,T,H", [
+    ("bf16", "bf16", "bf16", 8, False, 32, 128),   # 8 parts, 16-token blocks
+    ("bf16", "f32", "bf16", 4, True, 128, 128),    # history parts + current, 32-token blocks
+    ("f16", "f16", "f16", 2, False, 37, 16),       # ragged last token block
+    ("f32", "f32", "bf16", 0, True, 5, 8),         # a local part alone
+])
+def test_combine_vup_fused(pdt, ldt, dt, n, local, T, H):
+    """mla_combine_vup equals mla_lse_combine (latent in the compute type)
+    followed by mla_vup bit for bit (output, LSE, merged latent), and the
+    oracle's combine + V-up within the storage rounding."""
+    r = np.random.Generator(np.random.PCG64(123))
+    P = n + (1 if local else 0)
+    outs = r.standard_normal((P, T, H, 512)) * 0.1
+    lses = r.uniform(2, 12, size=(P, T, H))
+    lses[0, 0, :] = -np.inf                # empty part
+    outs[0, 0, :] = 0
+    lses[:, 1, 3] = -np.inf                # fully empty row
+    outs[:, 1, 3] = 0
+    lses[P - 1, 2, :] += 80.0              # extreme part
+    o_s = W.round_to(outs, pdt)
+    l_s = np.where(np.isfinite(lses), W.round_to(np.where(np.isfinite(lses), lses, 0), ldt), -np.inf)
+    wuv = W.round_to(r.standard_normal((H, 512, 128)) / math.sqrt(512), dt)
+    dev = "cuda"
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    tp = to_device(W.to_storage(o_s, pdt), pdt, dev)
+    tl = to_device(W.to_storage(l_s, ldt), ldt, dev)
+    tw = to_device(W.to_storage(wuv, dt), dt, dev)
+    parts = (tp[:n].contiguous(), tl[:n].contiguous()) if n else (None, None)
+    loc = dict(local_out=tp[n].contiguous(), local_lse=tl[n].contiguous()) if local else {}
+    # two calls
+    lat2 = torch.empty((T, H, 512), dtype=tdt, device=dev)
+    lse2 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    out2 = torch.empty((T, H, 128), dtype=tdt, device=dev)
+    L.mla_lse_combine(parts[0], parts[1], lat2, lse2, **loc)
+    L.mla_vup(lat2, tw, out2)
+    # fused, poisoned outputs first
+    lat = torch.full((T, H, 512), float("nan"), dtype=tdt, device=dev)
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.full((T, H, 128), float("nan"), dtype=tdt, device=dev)
+    L.mla_combine_vup(parts[0], parts[1], tw, out, lse, lat_out=lat, **loc)
+    out_nolat = torch.full((T, H, 128), float("nan"), dtype=tdt, device=dev)
+    L.mla_combine_vup(parts[0], parts[1], tw, out_nolat, None, **loc)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(out_nolat, out2)
+    assert torch.equal(lat, lat2)
+    assert torch.equal(torch.isnan(lse), torch.isnan(lse2)) and not torch.isnan(lse).any()
+    assert torch.equal(lse, lse2)
+    ref_o, ref_l = mo.lse_combine(o_s, l_s)
+    ref = mo.v_up(W.round_to(ref_o, dt), wuv)
+    go = f64(out)
+    assert np.all(np.abs(go - ref) <= half_ulp(ref, dt) + 1e-3)
+    fin = np.isfinite(ref_l)
+    assert np.all(f64(lse)[~fin] == -np.inf)
+    assert np.abs(f64(lse)[fin] - ref_l[fin]).max() <= 2e-5 * max(1.0, np.abs(ref_l[fin]).max())
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
 def test_vup_and_absorb(dt):
     r = np.random.Generator(np.random.PCG64(5))
