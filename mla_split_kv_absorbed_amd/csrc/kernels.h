@@ -37,7 +37,6 @@ hipError_t launch_partial_simple(const PartialParams& pp, int dtype, hipStream_t
 bool mfma_path_supported(int dtype, int H, int block_size);
 hipError_t launch_partial_mfma(const PartialParams& pp, int dtype, hipStream_t st);
 // Upper bound on split sub-ranges ("slots") an MFMA-path call may write.
-size_t mfma_max_slots(int B, int S, int P, int num_splits);
 size_t mfma_max_chunks(int B, int S, int P, int num_splits);
 size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits, int out_dtype);
 

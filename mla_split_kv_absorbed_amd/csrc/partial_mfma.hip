@@ -864,7 +864,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       for (int g = 0; g < kWaves; ++g) wb0[g] = wload(g, 0);
       va01[0] = vload(pl, 0, 0);
       va01[1] = vload(pl, 1, 0);
-      floatx16 none;
+      const floatx16 none = {};  // no softmax in this call: never read
       pv_group(3, cv, cw, 0, kWaves);
       pv(pl, std::integral_constant<bool, false>(), none, nullptr, wb0, va01, nullptr, nullptr);
     }
@@ -948,8 +948,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       __syncthreads();
       char* out = (char*)(dst + (size_t)half * 64 * kDc);
 #pragma unroll
-      for (int idx = tid; idx < 64 * kRowPieces; idx += 256) {
-        const int r = idx / kRowPieces, c = idx % kRowPieces;
+      for (int i = 0; i < 64 * kRowPieces / 256; ++i) {
+        const int idx = tid + i * 256, r = idx / kRowPieces, c = idx % kRowPieces;
         *(uint4*)(out + (size_t)r * kDc * kSz + c * 16) = *(const uint4*)(lds + r * kPitch + c * 16);
       }
       __syncthreads();
@@ -1064,8 +1064,6 @@ bool mfma_path_supported(int dtype, int H, int block_size) {
   return (dtype == MLA_BF16 || dtype == MLA_F16) && H == kHeadsGroup &&
          (block_size == 0 || block_size % kTile == 0);
 }
-
-size_t mfma_max_slots(int B, int S, int P, int hint) { return slots_bound(B, S, P, hint); }
 
 size_t mfma_max_chunks(int B, int S, int P, int hint) {
   const size_t U = (size_t)P * B;
