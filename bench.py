@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode µs/step, TFLOP/s & KV GB/s (% roofline) at B=32 H=128 L=32K"
 HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20   # MI355X Infinity Cache
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 KERNEL_SRCS = [os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", f)
                for f in ("partial_mfma.hip", "common.h", "kernels.h")]
@@ -106,6 +107,9 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=150)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="independent KV caches rotated over the steps (0 = enough to exceed "
+                         "twice the 256 MB Infinity Cache when one cache is smaller)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--copy-probe", action="store_true",
@@ -139,26 +143,35 @@ def main():
     sp = W.SPECS[args.workload]
     print(f"[bench] generating workload {sp.name}", file=sys.stderr, flush=True)
     w = W.make_workload(sp)
-    st = DecodeStep(w, device="cuda:0")
     work = W.step_work(w)
+    # Cold-cache discipline: a cache smaller than twice the 256 MB Infinity
+    # Cache (MALL) would stay resident across steps, so enough independent
+    # copies are rotated that the steps touch more than 512 MB in turn.
+    kv_bytes = w.kv.nbytes
+    copies = args.copies or (1 if kv_bytes >= MALL_BYTES * 2 or kv_bytes < 16 << 20
+                             else -(-(2 * MALL_BYTES) // kv_bytes) + 1)
+    sts = [DecodeStep(w, device="cuda:0") for _ in range(copies)]
+    st = sts[0]
     stream = torch.cuda.current_stream()
 
-    # one shard alone: the first part's ranges, a single-part call
-    share = DecodeStep.__new__(DecodeStep)
-    one_args = L.partial_args(st.q_lat, st.q_rope, st.kv, st.range_start[:1].contiguous(),
-                              st.range_end[:1].contiguous(), st.parts_out[:1],
-                              st.parts_lse[:1], B=sp.B, S=sp.S, H=sp.H, scale=sp.scale,
-                              **({"block_table": st.block_table, "block_size": sp.block_size,
-                                  "num_blocks": w.kv.shape[0]} if sp.block_size else
-                                 {"kv_seq_stride": w.kv.shape[1]}))
-    one_ws = torch.empty(max(1, L.mla_decode_partial_workspace_size(one_args)),
-                         dtype=torch.uint8, device="cuda:0")
-    one_args.workspace, one_args.workspace_bytes = one_ws.data_ptr(), one_ws.numel()
-    del share
+    # one DCP rank's share: each part alone, a single-part call per part
+    def share_args(p):
+        a = L.partial_args(st.q_lat, st.q_rope, st.kv, st.range_start[p:p + 1].contiguous(),
+                           st.range_end[p:p + 1].contiguous(), st.parts_out[p:p + 1],
+                           st.parts_lse[p:p + 1], B=sp.B, S=sp.S, H=sp.H, scale=sp.scale,
+                           **({"block_table": st.block_table, "block_size": sp.block_size,
+                               "num_blocks": w.kv.shape[0]} if sp.block_size else
+                              {"kv_seq_stride": w.kv.shape[1]}))
+        ws_ = torch.empty(max(1, L.mla_decode_partial_workspace_size(a)), dtype=torch.uint8,
+                          device="cuda:0")
+        a.workspace, a.workspace_bytes = ws_.data_ptr(), ws_.numel()
+        return a, ws_
+    shares = [share_args(p) for p in range(sp.parts)]
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        st.run(stream)
+    print(f"[bench] warmup ({copies} cache cop{'y' if copies == 1 else 'ies'})",
+          file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        sts[i % copies].run(stream)
     torch.cuda.synchronize()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -170,6 +183,7 @@ def main():
     e_end = torch.cuda.Event(enable_timing=True)
     e_start.record(stream)
     for i in range(args.steps):
+        st = sts[i % copies]
         if st.absorb:
             L.mla_q_absorb(st.q_nope, st.w_uk, st.q_lat, stream)
         ev[i][0].record(stream)
@@ -196,17 +210,24 @@ def main():
     ms_step = e_start.elapsed_time(e_end) / args.steps
     part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
 
-    # one rank's share, timed alone
+    # each rank's share timed alone, the parts called in turn (each call
+    # meets its part's keys cold: the other parts' keys came in between)
+    rounds = max(10, args.steps // sp.parts)
     for _ in range(3):
-        L.mla_decode_partial(one_args, stream)
+        for a, _ws in shares:
+            L.mla_decode_partial(a, stream)
+    sev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(rounds)] for _ in shares]
+    for r in range(rounds):
+        for p, (a, _ws) in enumerate(shares):
+            sev[p][r][0].record(stream)
+            L.mla_decode_partial(a, stream)
+            sev[p][r][1].record(stream)
     torch.cuda.synchronize()
-    e1, e2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e1.record(stream)
-    for _ in range(args.steps):
-        L.mla_decode_partial(one_args, stream)
-    e2.record(stream)
-    torch.cuda.synchronize()
-    share_us = e1.elapsed_time(e2) / args.steps * 1e3
+    share_per_part = [float(np.mean([e0.elapsed_time(e1) for e0, e1 in sev[p]])) * 1e3
+                      for p in range(len(shares))]
+    share_us = float(np.mean(share_per_part))
+    st = sts[0]
 
     us = ms_step * 1e3
     tflops = work["total_flops"] / (us * 1e-6) / 1e12
@@ -216,7 +237,15 @@ def main():
     bound_step = ("hbm" if work["total_bytes"] / (HBM_PEAK_GBS * 1e9) >=
                   work["total_flops"] / (MFMA_PEAK_TFLOPS[sp.dtype] * 1e12) else "mfma")
     part_bytes = work["partial_bytes"]
-    achieved = part_bytes / (part_ms * 1e-3) / 1e9
+    # the partial kernel's own bound: bytes at the HBM peak or matrix work at
+    # the MFMA peak, whichever takes longer
+    part_mfma = work["attn_flops"] / (MFMA_PEAK_TFLOPS[sp.dtype] * 1e12) > part_bytes / (
+        HBM_PEAK_GBS * 1e9)
+    if part_mfma:
+        achieved, peak, unit = work["attn_flops"] / (part_ms * 1e-3) / 1e12, \
+            MFMA_PEAK_TFLOPS[sp.dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = part_bytes / (part_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
     wl = f"config{sp.wid}:{sp.name}"
     traffic = traffic_from_profile(wl)
     res = {
@@ -242,12 +271,14 @@ def main():
                           "algorithmic_bytes": work["total_bytes"],
                           "algorithmic_flops": work["total_flops"]},
         "roofline": {"kernel": "partial_mfma_kernel (mla_decode_partial, all parts)",
-                     "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bound": "mfma" if part_mfma else "hbm", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "bytes_per_launch": part_bytes,
                      "avg_launch_us": round(part_ms * 1e3, 2),
                      "mfma_tflops": round(work["attn_flops"] / (part_ms * 1e-3) / 1e12, 1)},
         "one_rank_share_us": round(share_us, 2),
+        "one_rank_share_per_part_us": [round(x, 2) for x in share_per_part],
+        "kv_cache_copies": copies,
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:
