@@ -45,8 +45,8 @@ template <> struct GT<f16> {
 };
 
 // ---------------------------------------------------------------------------
-// q absorption: grid (H, 2 halves of c, ceil(T/32)), 4 waves, each wave two
-// 32-row c tiles of one 32-token block.
+// q absorption of one 32-token block (the fused prologue's grid: (H, 2
+// halves of c, ceil(T/32))), 4 waves, each wave two 32-row c tiles.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void absorb_block(const T* __restrict__ qn, const T* __restrict__ wuk,
@@ -101,11 +101,66 @@ __device__ __forceinline__ void absorb_block(const T* __restrict__ qn, const T* 
   }
 }
 
+// q absorption over many token blocks: grid (H, 2 halves of c, ceil(blocks /
+// kAbsorbBlocks)); each wave keeps its two W_UK tiles in registers and walks
+// up to kAbsorbBlocks 32-token blocks, loading the next block's q_nope while
+// the current one is multiplied, so W_UK[h] is read once per kAbsorbBlocks
+// blocks instead of once per block.
+constexpr int kAbsorbBlocks = 4;
+
 template <typename T>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ qn,
                                                           const T* __restrict__ wuk,
                                                           T* __restrict__ ql, int Tn, int H) {
-  absorb_block<T>(qn, wuk, ql, Tn, H);
+  typedef typename GT<T>::v8 v8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = blockIdx.x;
+  const int c0 = blockIdx.y * 256 + wave * 64;
+  const int r = lane & 31, hi = lane >> 5;
+  const int nblk = (Tn + 31) / 32;
+  const int b0 = blockIdx.z * kAbsorbBlocks, b1 = min(nblk, b0 + kAbsorbBlocks);
+  // B = q_nope^T of block tb: column t, 8 consecutive j per k step (rows past
+  // Tn load the last valid row and are never stored)
+  auto load_b = [&](int tb, v8* b) __attribute__((always_inline)) {
+    const int tl = min(tb * 32 + r, Tn - 1);
+#pragma unroll
+    for (int k = 0; k < kDn / 16; ++k)
+      b[k] = *(const v8*)(qn + ((size_t)tl * H + h) * kDn + k * 16 + hi * 8);
+  };
+  v8 a[2][kDn / 16];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const T* wr = wuk + ((size_t)h * kDc + c0 + ct * 32 + r) * kDn + hi * 8;
+#pragma unroll
+    for (int k = 0; k < kDn / 16; ++k) a[ct][k] = *(const v8*)(wr + k * 16);
+  }
+  v8 b[2][kDn / 16];
+  load_b(b0, b[0]);
+#pragma unroll
+  for (int i = 0; i < kAbsorbBlocks; ++i) {
+    const int tb = b0 + i;
+    if (tb >= b1) break;
+    if (tb + 1 < b1) load_b(tb + 1, b[(i + 1) & 1]);
+    const int t = tb * 32 + r;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      floatx16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int k = 0; k < kDn / 16; ++k) acc = GT<T>::mfma(a[ct][k], b[i & 1][k], acc);
+      if (t < Tn) {
+        T* dst = ql + ((size_t)t * H + h) * kDc + c0 + ct * 32 + 4 * hi;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          typename GT<T>::v4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (T)acc[4 * g + e];
+          *(typename GT<T>::v4*)(dst + 8 * g) = v;
+        }
+      }
+    }
+  }
 }
 
 // The fused decode prologue: the absorption blocks (head, c half, token
@@ -198,7 +253,7 @@ static_assert(kVupChunks * kVupThreads * 16 == kDc * kVupCols * 2, "V-up staging
 
 hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int Tn, int H, int dt,
                               hipStream_t st) {
-  dim3 g(H, kDc / 256, (Tn + 31) / 32);
+  dim3 g(H, kDc / 256, ((Tn + 31) / 32 + kAbsorbBlocks - 1) / kAbsorbBlocks);
   if (dt == MLA_BF16)
     hipLaunchKernelGGL(absorb_mfma_kernel<bf16>, g, dim3(256), 0, st, (const bf16*)qn,
                        (const bf16*)w, (bf16*)ql, Tn, H);
