@@ -60,6 +60,62 @@ def traffic_from_profile(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+PMC_GRID = 65536  # grid of the 8-part decode-step launch of the 32K workload
+
+
+def _pmc_rows(run_dir: str, counter: str):
+    import csv
+    path = os.path.join(run_dir, "run_counter_collection.csv")
+    with open(path) as f:
+        return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+
+
+def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
+    """HBM traffic per launch of the partial kernel from two rocprofv3 --pmc
+    runs of the decode step (FETCH_SIZE, then WRITE_SIZE, in KiB per
+    dispatch), each scaled by what the same counter reads for a plain device
+    copy of known size (the copy probe)."""
+    def kern_mean(d, c):
+        v = [float(r["Counter_Value"]) for r in _pmc_rows(d, c)
+             if "partial_mfma_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == PMC_GRID]
+        if not v:
+            raise SystemExit(f"no partial_mfma_kernel dispatch of grid {PMC_GRID} in {d}")
+        return sum(v) / len(v), len(v)
+
+    def copy_mean(d, c):
+        rows = [r for r in _pmc_rows(d, c) if "copy" in r["Kernel_Name"].lower()]
+        big = max(int(r["Grid_Size"]) for r in rows)
+        v = [float(r["Counter_Value"]) for r in rows if int(r["Grid_Size"]) == big]
+        return sum(v) / len(v)
+
+    fetch, nf = kern_mean(fetch_dir, "FETCH_SIZE")
+    write, nw = kern_mean(write_dir, "WRITE_SIZE")
+    n_copy = 2 * 256 * 1024 * 1024  # bytes read and written by the copy probe
+    cf, cw = copy_mean(copy_fetch_dir, "FETCH_SIZE"), copy_mean(copy_write_dir, "WRITE_SIZE")
+    ff, wf = n_copy / (cf * 1024), n_copy / (cw * 1024)
+    rd, wr = fetch * 1024 * ff, write * 1024 * wf
+    return {
+        "kernel": "partial_mfma_kernel<bf16>",
+        "workload": "config2:bf16_B32_H128_L32768_paged32_8parts",
+        "kernel_sha": kernel_hash(),
+        "kernel_sha_of": "bench.kernel_hash(): partial_mfma.hip, common.h and kernels.h with "
+                         "comments and blank lines dropped",
+        "fetch_kib_per_dispatch": round(fetch, 3),
+        "write_kib_per_dispatch": round(write, 3),
+        "dispatches": {"fetch": nf, "write": nw},
+        "copy_probe": {"bytes_read": n_copy, "bytes_written": n_copy,
+                       "fetch_kib": round(cf, 3), "write_kib": round(cw, 3)},
+        "fetch_factor": round(ff, 4),
+        "write_factor": round(wf, 4),
+        "hbm_read_bytes_per_launch": int(rd),
+        "hbm_write_bytes_per_launch": int(wr),
+        "hbm_bytes_per_launch": int(rd + wr),
+        "commands": commands,
+        "note": f"partial_mfma_kernel dispatches with grid {PMC_GRID} (the 8-part decode-step "
+                "launch) only; the copy probe is the device copy of 512 MiB",
+    }
+
+
 def cpu_baseline(w, budget_s: float = 15.0):
     """The float64 oracle on a bounded sample of (sequence, head) pairs of the
     same workload, scaled to microseconds per full step."""
@@ -115,7 +171,40 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain device copy of 512 MiB three times (the "
                          "calibration kernel for the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only run the device peak microbenchmarks (HBM read and copy, bf16 "
+                         "matrix cores, LDS reads) and print them beside the published peaks")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR",
+                                                       "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the partial kernel's HBM traffic file from four rocprofv3 "
+                         "--pmc output directories (no GPU needed)")
     args = ap.parse_args()
+    if args.pmc_summary:
+        dirs = args.pmc_summary
+        cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py "
+                + ("--copy-probe" if i >= 2 else "--steps 2 --warmup 1 --no-cpu-baseline")
+                for i, (c, d) in enumerate(zip(("FETCH_SIZE", "WRITE_SIZE") * 2, dirs))]
+        res = pmc_summary(*dirs, cmds)
+        with open(PMC_FILE, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+        print(json.dumps(res), flush=True)
+        return
+    if args.peaks:
+        from mla_split_kv_absorbed_amd import build as B
+        if not os.path.exists(B.PEAKS_BIN):
+            print(f"bench.py: {B.PEAKS_BIN} is not built", file=sys.stderr)
+            sys.exit(1)
+        import subprocess
+        r = subprocess.run([B.PEAKS_BIN], stdout=subprocess.PIPE, text=True)
+        if r.returncode != 0:
+            sys.exit(r.returncode)
+        meas = json.loads(r.stdout.strip().splitlines()[-1])
+        print(json.dumps({"measured": meas,
+                          "published": {"hbm_gbs": HBM_PEAK_GBS,
+                                        "mfma_bf16_tflops": MFMA_PEAK_TFLOPS["bf16"],
+                                        "clock_ghz": 2.4, "compute_units": 256}}), flush=True)
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "the DCP parts are processed on the one device", file=sys.stderr)

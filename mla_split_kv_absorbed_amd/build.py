@@ -13,6 +13,9 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libmla_decode.so")
+# the device peak microbenchmarks (HBM, matrix cores, LDS), a separate program
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS_BIN = os.path.join(PKG, "peaks", "mla_peaks")
 ARCH = "gfx950"
 
 # Per-source extra hipcc flags, by file name (none needed at present).
@@ -48,7 +51,11 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         if len(procs) >= jobs:
             _drain(procs)
+    # the peak microbenchmark program, built alongside
+    cmd = [hipcc(), PEAKS_SRC, "-o", PEAKS_BIN + ".tmp"] + [a for a in common if a != "-fPIC"]
+    procs.append((PEAKS_SRC, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
     _drain(procs)
+    os.replace(PEAKS_BIN + ".tmp", PEAKS_BIN)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-o", tmp] + objs + [f"--offload-arch={ARCH}", "-fPIC"]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)

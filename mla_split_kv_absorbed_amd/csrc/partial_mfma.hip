@@ -44,8 +44,7 @@
 // tile j's weights go to LDS between the instructions of one more value
 // group, and the last group is carried across the next barrier so the matrix
 // unit has work while the first key operands load. The loads of tile j + 2
-// are spread over the value product: the score product's key reads (4 waves
-// x 36 KB per tile) already keep the LDS near its read bandwidth.
+// are spread over the score product.
 //
 // Ranges that need splitting (few sequences, long ranges) are cut into
 // chunks; chunk results go to a fp32 workspace and a second kernel merges
@@ -647,8 +646,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   // between, so their vector work runs in the shadow of the
   // matrix instructions; they are returned packed in `pk`.
   auto pv = [&](const char* pb, auto soft, const floatx16& sa, t2* pk, const v8* wb0,
-                const v8* va01, v8* wb1_out, v8* va67_out, auto issue)
-      __attribute__((always_inline)) {
+                const v8* va01, v8* wb1_out, v8* va67_out) __attribute__((always_inline)) {
     constexpr bool kSoft = decltype(soft)::value;
     // weight of score i: 2^(s * sl2 - m_ref) with s = sa[i]; pairs
     // are packed to the matrix input type. The output is normalised by the
@@ -690,11 +688,6 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
         // the 16 weights spread over instructions 4..23 (4 of every 5
         // slots): the first 4 cover the score product's result latency
         if constexpr (kSoft) {
-          // the LDS-direct loads of tile j + 2, spread over the first 22
-          // instructions (the score product already keeps the LDS busy)
-#pragma unroll
-          for (int i = 0; i < kLoadsWave; ++i)
-            if (4 * n + g == (8 * i) / 3) issue(i);
           const int m = 4 * n + g - 4;
           if (m >= 0 && m % 5 != 4) weight(m - m / 5);
           __builtin_amdgcn_sched_barrier(0);
@@ -736,8 +729,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     __syncthreads();
     // the loads of tile j + kAheadTiles go into the stage of tile j - 2,
     // which every wave finished reading before this barrier; they are
-    // spread over the value product, whose LDS traffic is light, while the
-    // score product's key reads keep the LDS busy
+    // spread over the score product so the CU's address unit drains them
+    // while the matrix unit works
     const bool do_issue = j + kAheadTiles < seg_end;
     __amdgpu_buffer_rsrc_t nrs = tile_rsrc(do_issue ? j + kAheadTiles : te, next_id);
     const unsigned nm0 =
@@ -783,6 +776,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       else
         MT<T>::qk_next(sacc, kb[n % kRing], q[n]);
       if (n + kAhead < kKSteps) kb[(n + kAhead) % kRing] = *kaddr(n + kAhead);
+      if ((n & 3) == 2) issue_part(n >> 2);  // n = 2, 6, ..., 34: loads 0..8
       // first operands of the value product, in the last three slots
       // (harmless reads of stale data when there is no previous tile)
       if (n == kKSteps - 3)
@@ -811,11 +805,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     t2 pk[8];
     v8 va67[2];
     if (has_prev) {
-      pv(pb, std::integral_constant<bool, true>(), sacc, pk, wb0, va01, cw, va67, issue_part);
+      pv(pb, std::integral_constant<bool, true>(), sacc, pk, wb0, va01, cw, va67);
     } else {
       // first tile of a segment: the weights alone (same arithmetic)
-#pragma unroll
-      for (int i = 0; i < kLoadsWave; ++i) issue_part(i);
       qk_drain(sacc);
       float pf_even = 0.f;
 #pragma unroll
@@ -874,8 +866,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       va01[1] = vload(pl, 1, 0);
       const floatx16 none = {};  // no softmax in this call: never read
       pv_group(3, cv, cw, 0, kWaves);
-      pv(pl, std::integral_constant<bool, false>(), none, nullptr, wb0, va01, nullptr, nullptr,
-         [](int) {});
+      pv(pl, std::integral_constant<bool, false>(), none, nullptr, wb0, va01, nullptr, nullptr);
     }
     // the last steps' loads (no records: they only zero consumed stages)
     // land before the workgroup moves on or ends

@@ -1,0 +1,212 @@
+// Achievable peaks of the device, measured with small dedicated kernels, for
+// the roofline figures of the decode path (the published MI355X peaks are
+// reported beside them):
+//   - HBM: a streaming read of a 2 GiB buffer, and a copy of 1 GiB;
+//   - matrix cores: independent bf16 32x32x16 products, one wave per SIMD;
+//   - LDS: 16-byte reads (the key operand form) and 8-byte transposed reads
+//     (the value operand form), four waves per compute unit.
+// One JSON object is printed on stdout. Every kernel is launched on all
+// compute units; LDS and HBM addresses stay inside their buffers.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <vector>
+
+#define CHECK(x)                                                              \
+  do {                                                                        \
+    hipError_t e_ = (x);                                                      \
+    if (e_ != hipSuccess) {                                                   \
+      fprintf(stderr, "%s failed: %s\n", #x, hipGetErrorString(e_));          \
+      exit(1);                                                                \
+    }                                                                         \
+  } while (0)
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// ---- HBM -------------------------------------------------------------------
+__global__ __launch_bounds__(256) void read_kernel(const float4* __restrict__ src, size_t n,
+                                                   float* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  float acc = 0.f;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + 3 * stride < n; i += 4 * stride) {
+    const float4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+    acc += (a.x + b.y) + (c.z + d.w);
+  }
+  for (; i < n; i += stride) acc += src[i].x;
+  out[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(256) void copy_kernel(const float4* __restrict__ src,
+                                                   float4* __restrict__ dst, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
+}
+
+// ---- matrix cores ----------------------------------------------------------
+constexpr int kMfmaIters = 4096;
+
+__device__ __forceinline__ unsigned long long clk() {
+  unsigned long long v;
+  asm volatile("s_memtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v)::"memory");
+  return v;
+}
+
+__global__ __launch_bounds__(256, 1) void mfma_kernel(float* out, unsigned long long* cyc) {
+  bf16x8 a, b;
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (threadIdx.x & 7));
+    b[i] = (__bf16)0.002f;
+  }
+  floatx16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const unsigned long long t0 = clk();
+  for (int it = 0; it < kMfmaIters; ++it) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  const unsigned long long t1 = clk();
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += c0[i] + c1[i] + c2[i] + c3[i];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  if (threadIdx.x == 0) cyc[blockIdx.x] = t1 - t0;
+}
+
+// ---- LDS -------------------------------------------------------------------
+constexpr int kLdsBytes = 128 * 1024;
+constexpr int kLdsIters = 2048;
+
+// TR = false: ds_read_b128 (16 B per lane); TR = true: ds_read_b64_tr_b16
+// (8 B per lane). 8 reads in flight per wave; addresses are masked into the
+// buffer and rotate through it.
+template <bool TR>
+__global__ __launch_bounds__(256, 1) void lds_kernel(float* out, unsigned long long* cyc) {
+  __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < kLdsBytes / 4; i += 256) ((float*)lds)[i] = (float)(i & 7);
+  __syncthreads();
+  float s = 0.f;
+  const unsigned long long t0 = clk();
+  for (int it = 0; it < kLdsIters; ++it) {
+    if constexpr (!TR) {
+      bf16x8 r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        r[i] = *(const LDS_AS bf16x8*)(lds + ((wave * 16384 + lane * 16 + i * 1024 + it * 128) &
+                                              (kLdsBytes - 1)));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(r[i]));
+    } else {
+      shortx4 r[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        r[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS shortx4*)(lds + ((wave * 16384 + lane * 8 + i * 512 + it * 128) &
+                                     (kLdsBytes - 1))));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(r[i]));
+    }
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const unsigned long long t1 = clk();
+  out[blockIdx.x * blockDim.x + tid] = s;
+  if (tid == 0) cyc[blockIdx.x] = t1 - t0;
+}
+
+// ---- host ------------------------------------------------------------------
+template <typename F>
+static float best_ms(F launch, int reps) {
+  hipEvent_t e0, e1;
+  CHECK(hipEventCreate(&e0));
+  CHECK(hipEventCreate(&e1));
+  launch();  // warm-up
+  CHECK(hipDeviceSynchronize());
+  float best = 1e30f;
+  for (int r = 0; r < reps; ++r) {
+    CHECK(hipEventRecord(e0));
+    launch();
+    CHECK(hipEventRecord(e1));
+    CHECK(hipEventSynchronize(e1));
+    float ms;
+    CHECK(hipEventElapsedTime(&ms, e0, e1));
+    if (ms < best) best = ms;
+  }
+  CHECK(hipEventDestroy(e0));
+  CHECK(hipEventDestroy(e1));
+  return best;
+}
+
+static double mean_cycles(const unsigned long long* d, int n) {
+  std::vector<unsigned long long> h(n);
+  CHECK(hipMemcpy(h.data(), d, n * sizeof(unsigned long long), hipMemcpyDeviceToHost));
+  double s = 0;
+  for (int i = 0; i < n; ++i) s += (double)h[i];
+  return s / n;
+}
+
+int main() {
+  hipDeviceProp_t prop;
+  CHECK(hipGetDeviceProperties(&prop, 0));
+  const int cus = prop.multiProcessorCount;
+
+  // HBM: 2 GiB read, 1 GiB -> 1 GiB copy
+  const size_t rbytes = (size_t)2 << 30, cbytes = (size_t)1 << 30;
+  float4 *src, *dst;
+  float* sink;
+  CHECK(hipMalloc(&src, rbytes));
+  CHECK(hipMalloc(&dst, cbytes));
+  CHECK(hipMemset(src, 0, rbytes));
+  const int grid = cus * 8;
+  CHECK(hipMalloc(&sink, (size_t)grid * 256 * sizeof(float)));
+  const float ms_read = best_ms([&] {
+    hipLaunchKernelGGL(read_kernel, dim3(grid), dim3(256), 0, 0, src, rbytes / 16, sink);
+  }, 10);
+  const float ms_copy = best_ms([&] {
+    hipLaunchKernelGGL(copy_kernel, dim3(grid), dim3(256), 0, 0, src, dst, cbytes / 16);
+  }, 10);
+  CHECK(hipGetLastError());
+
+  // matrix cores: one workgroup of 4 waves per compute unit
+  unsigned long long* cyc;
+  CHECK(hipMalloc(&cyc, (size_t)cus * sizeof(unsigned long long)));
+  const float ms_mfma = best_ms([&] {
+    hipLaunchKernelGGL(mfma_kernel, dim3(cus), dim3(256), 0, 0, sink, cyc);
+  }, 5);
+  const double mfma_cyc = mean_cycles(cyc, cus);
+  const double mfma_flop = (double)cus * 4 /*waves*/ * kMfmaIters * 4 * 32.0 * 32 * 16 * 2;
+
+  const float ms_lds = best_ms([&] {
+    hipLaunchKernelGGL(lds_kernel<false>, dim3(cus), dim3(256), 0, 0, sink, cyc);
+  }, 5);
+  const double lds_cyc = mean_cycles(cyc, cus);
+  const float ms_tr = best_ms([&] {
+    hipLaunchKernelGGL(lds_kernel<true>, dim3(cus), dim3(256), 0, 0, sink, cyc);
+  }, 5);
+  const double tr_cyc = mean_cycles(cyc, cus);
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
+
+  const double lds_bytes_cu = 4.0 * kLdsIters * 8 * 1024;  // per CU per launch
+  const double tr_bytes_cu = 4.0 * kLdsIters * 8 * 512;
+  printf("{\"device\": \"%s\", \"compute_units\": %d, "
+         "\"hbm_read_gbs\": %.1f, \"hbm_copy_gbs\": %.1f, "
+         "\"mfma_bf16_tflops\": %.1f, \"mfma_cycles_per_32x32x16\": %.2f, "
+         "\"mfma_clock_ghz\": %.3f, "
+         "\"lds_b128_bytes_per_clk_cu\": %.1f, \"lds_tr_b64_bytes_per_clk_cu\": %.1f, "
+         "\"lds_b128_tbs\": %.1f, \"lds_tr_b64_tbs\": %.1f}\n",
+         prop.gcnArchName, cus, rbytes / (ms_read * 1e-3) / 1e9,
+         2.0 * cbytes / (ms_copy * 1e-3) / 1e9, mfma_flop / (ms_mfma * 1e-3) / 1e12,
+         mfma_cyc / (kMfmaIters * 4.0), mfma_cyc / (ms_mfma * 1e6),
+         lds_bytes_cu / lds_cyc, tr_bytes_cu / tr_cyc,
+         lds_bytes_cu * cus / (ms_lds * 1e-3) / 1e12, tr_bytes_cu * cus / (ms_tr * 1e-3) / 1e12);
+  CHECK(hipFree(src));
+  CHECK(hipFree(dst));
+  CHECK(hipFree(sink));
+  CHECK(hipFree(cyc));
+  return 0;
+}
