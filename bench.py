@@ -116,6 +116,63 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
     }
 
 
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_LDS "
+    "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE",
+    "SQ_INSTS_VALU_MFMA_BF16 SQ_INSTS_VALU SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_ANY "
+    "SQ_WAIT_INST_ANY SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_LDS SQ_INSTS_SALU GRBM_GUI_ACTIVE",
+)
+
+
+def sq_summary(dirs):
+    """Matrix-core and LDS counters of the partial kernel's 8-part launch,
+    from rocprofv3 --pmc runs of the SQ_PASSES counter sets, as markdown."""
+    import csv
+    vals, durs = {}, []
+    for d in dirs:
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            rows = [r for r in csv.DictReader(f) if "partial_mfma_kernel" in r["Kernel_Name"]
+                    and int(r["Grid_Size"]) == PMC_GRID]
+        if not rows:
+            raise SystemExit(f"no partial_mfma_kernel dispatch of grid {PMC_GRID} in {d}")
+        per = {}
+        for r in rows:
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            durs.append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        for c, v in per.items():
+            vals.setdefault(c, sum(v) / len(v))
+    us = sum(durs) / len(durs)
+    simds, xcds = 256 * 4, 8
+    waves = 256 * 4
+    kTilesPerUnit = 4096 // 32  # tiles per (part, sequence) range of the 32K workload
+    clk = vals["GRBM_GUI_ACTIVE"] / xcds / us * 1e-3  # GHz; the counter sums the 8 XCDs
+    kcyc = vals["GRBM_GUI_ACTIVE"] / xcds
+    mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
+    flops = vals["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+    lines = [
+        "| counter | per launch |", "|---|---:|"] + [
+        f"| `{c}` | {v:,.0f} |" for c, v in sorted(vals.items())] + [
+        "", "| derived | value |", "|---|---:|",
+        f"| kernel duration (mean over the profiled launches) | {us:.1f} us |",
+        f"| core clock (GRBM_GUI_ACTIVE / 8 XCDs / duration) | {clk:.2f} GHz |",
+        f"| matrix-core busy cycles per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024) | {mfma_busy:,.0f} |",
+        f"| matrix-core busy fraction (/ kernel cycles {kcyc:,.0f}) | {mfma_busy / kcyc:.3f} |",
+        f"| bf16 matrix FLOPs (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) | {flops / 1e9:.1f} GFLOP |",
+        f"| matrix rate | {flops / (us * 1e-6) / 1e12:.0f} TFLOP/s = "
+        f"{flops / (us * 1e-6) / 2.5e15:.3f} of 2.5 PFLOP/s, "
+        f"{flops / (us * 1e-6) / (2.5e15 * clk / 2.4):.3f} of the peak at {clk:.2f} GHz |",
+        f"| cycles per matrix instruction issued (busy / count per SIMD) | "
+        f"{mfma_busy / (vals['SQ_INSTS_VALU_MFMA_BF16'] / simds):.1f} |",
+        f"| LDS instructions per wave | {vals['SQ_INSTS_LDS'] / waves:,.0f} |",
+        f"| LDS bank-conflict cycles per wave and 32-token tile (SQ_LDS_BANK_CONFLICT / 1024 "
+        f"waves / {kTilesPerUnit} tiles) | "
+        f"{vals['SQ_LDS_BANK_CONFLICT'] / waves / kTilesPerUnit:.1f} |",
+        f"| wave cycles waiting on a counter (SQ_WAIT_ANY / SQ_WAVE_CYCLES) | "
+        f"{vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.3f} |",
+    ]
+    return "\n".join(lines) + "\n"
+
+
 def cpu_baseline(w, budget_s: float = 15.0):
     """The float64 oracle on a bounded sample of (sequence, head) pairs of the
     same workload, scaled to microseconds per full step."""
@@ -178,7 +235,13 @@ def main():
                                                        "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the partial kernel's HBM traffic file from four rocprofv3 "
                          "--pmc output directories (no GPU needed)")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
+                    help="print the partial kernel's matrix-core and LDS counters (two rocprofv3 "
+                         "--pmc runs of the SQ_PASSES sets) as markdown (no GPU needed)")
     args = ap.parse_args()
+    if args.sq_summary:
+        print(sq_summary(args.sq_summary), end="", flush=True)
+        return
     if args.pmc_summary:
         dirs = args.pmc_summary
         cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py "
