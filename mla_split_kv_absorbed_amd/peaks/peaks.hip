@@ -4,7 +4,12 @@
 //   - HBM: a streaming read of a 2 GiB buffer, and a copy of 1 GiB;
 //   - matrix cores: independent bf16 32x32x16 products, one wave per SIMD;
 //   - LDS: 16-byte reads (the key operand form) and 8-byte transposed reads
-//     (the value operand form), four waves per compute unit.
+//     (the value operand form), four waves per compute unit;
+//   - the score-product pattern of the partial-attention kernel in
+//     isolation: a dependent 32x32x16 chain accumulating in VGPRs, one
+//     16-byte key read per instruction fetched 8 instructions ahead, a 1 KB
+//     LDS-direct load every 4 instructions and a workgroup barrier every 36,
+//     four waves per compute unit.
 // One JSON object is printed on stdout. Every kernel is launched on all
 // compute units; LDS and HBM addresses stay inside their buffers.
 #include <hip/hip_runtime.h>
@@ -118,6 +123,63 @@ __global__ __launch_bounds__(256, 1) void lds_kernel(float* out, unsigned long l
   if (tid == 0) cyc[blockIdx.x] = t1 - t0;
 }
 
+// ---- score-product pattern -----------------------------------------------------
+constexpr int kChainIters = 1000;
+constexpr int kChainLds = 64 * 1024;
+
+// 64 lanes x 16 bytes from `rs` at voffset + soffset into LDS [m0, m0 + 1 KB)
+__device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned m0, int voffset,
+                                           int soffset) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voffset), "s"(rs), "s"(soffset)
+               : "memory");
+}
+
+__global__ __launch_bounds__(256, 1) void chain_kernel(float* out, unsigned long long* cyc,
+                                                       const char* src, int src_blocks) {
+  __shared__ __attribute__((aligned(1024))) char lds[kChainLds];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < kChainLds / 4; i += 256) ((float*)lds)[i] = 0.001f * (i & 7);
+  __syncthreads();
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, src_blocks * 1024, 0x00020000);
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(LDS_AS char*)lds);
+  bf16x8 b;
+  for (int i = 0; i < 8; ++i) b[i] = (__bf16)0.002f;
+  // reads come from the first 32 KB, the LDS-direct loads land in the second
+  const int base = wave * 8192 + lane * 16;
+  bf16x8 r[10];
+  for (int i = 0; i < 10; ++i) r[i] = *(const LDS_AS bf16x8*)(lds + ((base + i * 1024) & 32767));
+  floatx16 acc = {};
+  const unsigned long long t0 = clk();
+  for (int it = 0; it < kChainIters; ++it) {
+#pragma unroll
+    for (int n = 0; n < 36; ++n) {
+      // the operand register is refilled two instructions after its last use
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(r[n % 10]), "v"(b));
+      r[(n + 8) % 10] = *(const LDS_AS bf16x8*)(lds + ((base + ((n + 8) % 8) * 1024) & 32767));
+      if ((n & 3) == 2) {
+        const int blk = ((blockIdx.x * 4 + wave) * 9 * kChainIters + it * 9 + (n >> 2)) % src_blocks;
+        lds_load16(rs, ldsb + 32768 + wave * 8192 + ((n >> 2) & 7) * 1024, lane * 16, blk * 1024);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    asm volatile("s_waitcnt vmcnt(9)" ::: "memory");  // the previous step's loads
+    __syncthreads();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  const unsigned long long t1 = clk();
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += acc[i];
+  for (int i = 0; i < 10; ++i) s += (float)r[i][0];
+  out[blockIdx.x * blockDim.x + tid] = s;
+  if (lane == 0) cyc[blockIdx.x * 4 + wave] = t1 - t0;
+}
+
 // ---- host ------------------------------------------------------------------
 template <typename F>
 static float best_ms(F launch, int reps) {
@@ -189,6 +251,18 @@ int main() {
   }, 5);
   const double tr_cyc = mean_cycles(cyc, cus);
   CHECK(hipGetLastError());
+
+  // score-product pattern: LDS-direct loads stream from the read buffer
+  unsigned long long* ccyc;
+  CHECK(hipMalloc(&ccyc, (size_t)cus * 4 * sizeof(unsigned long long)));
+  const int src_blocks = 1 << 20;  // the first 1 GiB: block offsets stay below 2^30
+  static_assert(((size_t)1 << 30) <= ((size_t)2 << 30), "inside the read buffer");
+  best_ms([&] {
+    hipLaunchKernelGGL(chain_kernel, dim3(cus), dim3(256), 0, 0, sink, ccyc, (const char*)src,
+                       src_blocks);
+  }, 3);
+  const double chain_cyc = mean_cycles(ccyc, cus * 4) / (kChainIters * 36.0);
+  CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
 
   const double lds_bytes_cu = 4.0 * kLdsIters * 8 * 1024;  // per CU per launch
@@ -198,15 +272,18 @@ int main() {
          "\"mfma_bf16_tflops\": %.1f, \"mfma_cycles_per_32x32x16\": %.2f, "
          "\"mfma_clock_ghz\": %.3f, "
          "\"lds_b128_bytes_per_clk_cu\": %.1f, \"lds_tr_b64_bytes_per_clk_cu\": %.1f, "
-         "\"lds_b128_tbs\": %.1f, \"lds_tr_b64_tbs\": %.1f}\n",
+         "\"lds_b128_tbs\": %.1f, \"lds_tr_b64_tbs\": %.1f, "
+         "\"score_chain_cycles_per_mfma\": %.2f}\n",
          prop.gcnArchName, cus, rbytes / (ms_read * 1e-3) / 1e9,
          2.0 * cbytes / (ms_copy * 1e-3) / 1e9, mfma_flop / (ms_mfma * 1e-3) / 1e12,
          mfma_cyc / (kMfmaIters * 4.0), mfma_cyc / (ms_mfma * 1e6),
          lds_bytes_cu / lds_cyc, tr_bytes_cu / tr_cyc,
-         lds_bytes_cu * cus / (ms_lds * 1e-3) / 1e12, tr_bytes_cu * cus / (ms_tr * 1e-3) / 1e12);
+         lds_bytes_cu * cus / (ms_lds * 1e-3) / 1e12, tr_bytes_cu * cus / (ms_tr * 1e-3) / 1e12,
+         chain_cyc);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(sink));
   CHECK(hipFree(cyc));
+  CHECK(hipFree(ccyc));
   return 0;
 }
