@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256, 1) void lds_kernel(float* out, unsigned long l
 }
 
 // ---- score-product pattern -----------------------------------------------------
-constexpr int kChainIters = 1000;
+constexpr int kChainIters = 200;  // every wave reads its own 1.8 MB: no block is read twice
 constexpr int kChainLds = 64 * 1024;
 
 // 64 lanes x 16 bytes from `rs` at voffset + soffset into LDS [m0, m0 + 1 KB)
@@ -178,6 +178,40 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(float* out, unsigned long
   for (int i = 0; i < 10; ++i) s += (float)r[i][0];
   out[blockIdx.x * blockDim.x + tid] = s;
   if (lane == 0) cyc[blockIdx.x * 4 + wave] = t1 - t0;
+}
+
+// ---- HBM through LDS-direct loads ---------------------------------------------
+// The partial kernel's load mechanism alone: each workgroup streams 36 KB
+// tiles (9 loads of 1 KB per wave) into a 4-stage LDS ring, two tiles ahead,
+// with a wait and a barrier per tile and nothing else.
+constexpr int kStreamTiles = 64;  // tiles per workgroup and launch
+
+__global__ __launch_bounds__(256, 1) void lds_stream_kernel(unsigned long long* cyc,
+                                                            const char* src, int src_blocks) {
+  __shared__ __attribute__((aligned(1024))) char lds[4 * 36864];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, src_blocks * 1024, 0x00020000);
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(LDS_AS char*)lds);
+  const int first = blockIdx.x * kStreamTiles * 36;  // this workgroup's first 1 KB block
+  auto issue = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < 9; ++i)
+      lds_load16(rs, ldsb + (j & 3) * 36864 + (wave * 9 + i) * 1024, lane * 16,
+                 (first + j * 36 + wave * 9 + i) * 1024);
+  };
+  const unsigned long long t0 = clk();
+  issue(0);
+  issue(1);
+  for (int j = 0; j < kStreamTiles; ++j) {
+    issue(j + 2 < kStreamTiles ? j + 2 : j + 2 - kStreamTiles);  // the last two re-read
+    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    __syncthreads();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const unsigned long long t1 = clk();
+  if (tid == 0) cyc[blockIdx.x] = t1 - t0;
 }
 
 // ---- host ------------------------------------------------------------------
@@ -255,12 +289,26 @@ int main() {
   // score-product pattern: LDS-direct loads stream from the read buffer
   unsigned long long* ccyc;
   CHECK(hipMalloc(&ccyc, (size_t)cus * 4 * sizeof(unsigned long long)));
-  const int src_blocks = 1 << 20;  // the first 1 GiB: block offsets stay below 2^30
-  static_assert(((size_t)1 << 30) <= ((size_t)2 << 30), "inside the read buffer");
-  best_ms([&] {
+  const int src_blocks = (1 << 21) - 64;  // just under the 2 GiB read buffer, size fits an int
+  if ((size_t)cus * 4 * 9 * kChainIters > (size_t)src_blocks) {
+    fprintf(stderr, "score-chain source too small\n");
+    return 1;
+  }
+  const float ms_chain = best_ms([&] {
     hipLaunchKernelGGL(chain_kernel, dim3(cus), dim3(256), 0, 0, sink, ccyc, (const char*)src,
                        src_blocks);
   }, 3);
+  const double chain_bytes = (double)cus * 4 * 9 * 1024 * kChainIters;
+
+  if ((size_t)cus * kStreamTiles * 36 > (size_t)src_blocks) {
+    fprintf(stderr, "stream source too small\n");
+    return 1;
+  }
+  const float ms_stream = best_ms([&] {
+    hipLaunchKernelGGL(lds_stream_kernel, dim3(cus), dim3(256), 0, 0, cyc, (const char*)src,
+                       src_blocks);
+  }, 5);
+  const double stream_bytes = (double)cus * (kStreamTiles + 2) * 36 * 1024;
   const double chain_cyc = mean_cycles(ccyc, cus * 4) / (kChainIters * 36.0);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
@@ -273,13 +321,16 @@ int main() {
          "\"mfma_clock_ghz\": %.3f, "
          "\"lds_b128_bytes_per_clk_cu\": %.1f, \"lds_tr_b64_bytes_per_clk_cu\": %.1f, "
          "\"lds_b128_tbs\": %.1f, \"lds_tr_b64_tbs\": %.1f, "
-         "\"score_chain_cycles_per_mfma\": %.2f}\n",
+         "\"score_chain_cycles_per_mfma\": %.2f, \"score_chain_hbm_gbs\": %.1f, "
+         "\"score_chain_clock_ghz\": %.3f, \"hbm_read_lds_direct_gbs\": %.1f}\n",
          prop.gcnArchName, cus, rbytes / (ms_read * 1e-3) / 1e9,
          2.0 * cbytes / (ms_copy * 1e-3) / 1e9, mfma_flop / (ms_mfma * 1e-3) / 1e12,
          mfma_cyc / (kMfmaIters * 4.0), mfma_cyc / (ms_mfma * 1e6),
          lds_bytes_cu / lds_cyc, tr_bytes_cu / tr_cyc,
          lds_bytes_cu * cus / (ms_lds * 1e-3) / 1e12, tr_bytes_cu * cus / (ms_tr * 1e-3) / 1e12,
-         chain_cyc);
+         chain_cyc, chain_bytes / (ms_chain * 1e-3) / 1e9,
+         chain_cyc * kChainIters * 36.0 / (ms_chain * 1e6),
+         stream_bytes / (ms_stream * 1e-3) / 1e9);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(sink));
