@@ -182,10 +182,12 @@ __global__ __launch_bounds__(256, 1) void chain_kernel(float* out, unsigned long
 
 // ---- HBM through LDS-direct loads ---------------------------------------------
 // The partial kernel's load mechanism alone: each workgroup streams 36 KB
-// tiles (9 loads of 1 KB per wave) into a 4-stage LDS ring, two tiles ahead,
-// with a wait and a barrier per tile and nothing else.
+// tiles (9 loads of 1 KB per wave) into a 4-stage LDS ring, AHEAD tiles ahead
+// (the kernel uses 2), with a wait and a barrier per tile and nothing else.
+// Nothing reads the ring, so a stage is reused as soon as its tile landed.
 constexpr int kStreamTiles = 64;  // tiles per workgroup and launch
 
+template <int AHEAD>
 __global__ __launch_bounds__(256, 1) void lds_stream_kernel(unsigned long long* cyc,
                                                             const char* src, int src_blocks) {
   __shared__ __attribute__((aligned(1024))) char lds[4 * 36864];
@@ -202,11 +204,15 @@ __global__ __launch_bounds__(256, 1) void lds_stream_kernel(unsigned long long* 
                  (first + j * 36 + wave * 9 + i) * 1024);
   };
   const unsigned long long t0 = clk();
-  issue(0);
-  issue(1);
+#pragma unroll
+  for (int a = 0; a < AHEAD; ++a) issue(a);
   for (int j = 0; j < kStreamTiles; ++j) {
-    issue(j + 2 < kStreamTiles ? j + 2 : j + 2 - kStreamTiles);  // the last two re-read
-    asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    issue(j + AHEAD < kStreamTiles ? j + AHEAD : j + AHEAD - kStreamTiles);  // tail re-reads
+    // tile j has landed once at most AHEAD tiles (9 loads each) are outstanding
+    if constexpr (AHEAD == 1) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    if constexpr (AHEAD == 2) asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    if constexpr (AHEAD == 3) asm volatile("s_waitcnt vmcnt(27)" ::: "memory");
+    if constexpr (AHEAD == 4) asm volatile("s_waitcnt vmcnt(36)" ::: "memory");
     __syncthreads();
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -304,11 +310,17 @@ int main() {
     fprintf(stderr, "stream source too small\n");
     return 1;
   }
-  const float ms_stream = best_ms([&] {
-    hipLaunchKernelGGL(lds_stream_kernel, dim3(cus), dim3(256), 0, 0, cyc, (const char*)src,
-                       src_blocks);
-  }, 5);
-  const double stream_bytes = (double)cus * (kStreamTiles + 2) * 36 * 1024;
+  double stream_gbs[5] = {};
+  auto stream = [&](auto kernel, int ahead) {
+    const float ms = best_ms([&] {
+      hipLaunchKernelGGL(kernel, dim3(cus), dim3(256), 0, 0, cyc, (const char*)src, src_blocks);
+    }, 5);
+    stream_gbs[ahead] = (double)cus * (kStreamTiles + ahead) * 36 * 1024 / (ms * 1e-3) / 1e9;
+  };
+  stream(lds_stream_kernel<1>, 1);
+  stream(lds_stream_kernel<2>, 2);
+  stream(lds_stream_kernel<3>, 3);
+  stream(lds_stream_kernel<4>, 4);
   const double chain_cyc = mean_cycles(ccyc, cus * 4) / (kChainIters * 36.0);
   CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
@@ -322,7 +334,8 @@ int main() {
          "\"lds_b128_bytes_per_clk_cu\": %.1f, \"lds_tr_b64_bytes_per_clk_cu\": %.1f, "
          "\"lds_b128_tbs\": %.1f, \"lds_tr_b64_tbs\": %.1f, "
          "\"score_chain_cycles_per_mfma\": %.2f, \"score_chain_hbm_gbs\": %.1f, "
-         "\"score_chain_clock_ghz\": %.3f, \"hbm_read_lds_direct_gbs\": %.1f}\n",
+         "\"score_chain_clock_ghz\": %.3f, \"hbm_read_lds_direct_gbs\": %.1f, "
+         "\"hbm_read_lds_direct_gbs_by_tiles_in_flight\": [%.1f, %.1f, %.1f, %.1f]}\n",
          prop.gcnArchName, cus, rbytes / (ms_read * 1e-3) / 1e9,
          2.0 * cbytes / (ms_copy * 1e-3) / 1e9, mfma_flop / (ms_mfma * 1e-3) / 1e12,
          mfma_cyc / (kMfmaIters * 4.0), mfma_cyc / (ms_mfma * 1e6),
@@ -330,7 +343,7 @@ int main() {
          lds_bytes_cu * cus / (ms_lds * 1e-3) / 1e12, tr_bytes_cu * cus / (ms_tr * 1e-3) / 1e12,
          chain_cyc, chain_bytes / (ms_chain * 1e-3) / 1e9,
          chain_cyc * kChainIters * 36.0 / (ms_chain * 1e6),
-         stream_bytes / (ms_stream * 1e-3) / 1e9);
+         stream_gbs[2], stream_gbs[1], stream_gbs[2], stream_gbs[3], stream_gbs[4]);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(sink));
