@@ -144,7 +144,7 @@ def sq_summary(dirs):
     us = sum(durs) / len(durs)
     simds, xcds = 256 * 4, 8
     waves = 256 * 4
-    kTilesPerUnit = 4096 // 32  # tiles per (part, sequence) range of the 32K workload
+    tiles_per_unit = 4096 // 32  # tiles per (part, sequence) range of the 32K workload
     clk = vals["GRBM_GUI_ACTIVE"] / xcds / us * 1e-3  # GHz; the counter sums the 8 XCDs
     kcyc = vals["GRBM_GUI_ACTIVE"] / xcds
     mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
@@ -165,8 +165,8 @@ def sq_summary(dirs):
         f"{mfma_busy / (vals['SQ_INSTS_VALU_MFMA_BF16'] / simds):.1f} |",
         f"| LDS instructions per wave | {vals['SQ_INSTS_LDS'] / waves:,.0f} |",
         f"| LDS bank-conflict cycles per wave and 32-token tile (SQ_LDS_BANK_CONFLICT / 1024 "
-        f"waves / {kTilesPerUnit} tiles) | "
-        f"{vals['SQ_LDS_BANK_CONFLICT'] / waves / kTilesPerUnit:.1f} |",
+        f"waves / {tiles_per_unit} tiles) | "
+        f"{vals['SQ_LDS_BANK_CONFLICT'] / waves / tiles_per_unit:.1f} |",
         f"| wave cycles waiting on a counter (SQ_WAIT_ANY / SQ_WAVE_CYCLES) | "
         f"{vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.3f} |",
     ]
