@@ -125,16 +125,23 @@ SQ_PASSES = (
 
 
 def sq_summary(dirs):
-    """Matrix-core and LDS counters of the partial kernel's 8-part launch,
-    from rocprofv3 --pmc runs of the SQ_PASSES counter sets, as markdown."""
+    """Matrix-core and LDS counters of the partial kernel's decode-step launch
+    (the partial_mfma_kernel grid with the longest mean duration: the
+    all-parts history call), from rocprofv3 --pmc runs of the SQ_PASSES
+    counter sets, as markdown."""
     import csv
     vals, durs = {}, []
     for d in dirs:
         with open(os.path.join(d, "run_counter_collection.csv")) as f:
-            rows = [r for r in csv.DictReader(f) if "partial_mfma_kernel" in r["Kernel_Name"]
-                    and int(r["Grid_Size"]) == PMC_GRID]
+            rows = [r for r in csv.DictReader(f) if "partial_mfma_kernel" in r["Kernel_Name"]]
         if not rows:
-            raise SystemExit(f"no partial_mfma_kernel dispatch of grid {PMC_GRID} in {d}")
+            raise SystemExit(f"no partial_mfma_kernel dispatch in {d}")
+        by_grid = {}
+        for r in rows:
+            by_grid.setdefault(int(r["Grid_Size"]), []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        grid = max(by_grid, key=lambda g: sum(by_grid[g]) / len(by_grid[g]))
+        rows = [r for r in rows if int(r["Grid_Size"]) == grid]
         per = {}
         for r in rows:
             per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
@@ -143,8 +150,7 @@ def sq_summary(dirs):
             vals.setdefault(c, sum(v) / len(v))
     us = sum(durs) / len(durs)
     simds, xcds = 256 * 4, 8
-    waves = 256 * 4
-    tiles_per_unit = 4096 // 32  # tiles per (part, sequence) range of the 32K workload
+    waves = grid // 64
     clk = vals["GRBM_GUI_ACTIVE"] / xcds / us * 1e-3  # GHz; the counter sums the 8 XCDs
     kcyc = vals["GRBM_GUI_ACTIVE"] / xcds
     mfma_busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / simds
@@ -153,6 +159,7 @@ def sq_summary(dirs):
         "| counter | per launch |", "|---|---:|"] + [
         f"| `{c}` | {v:,.0f} |" for c, v in sorted(vals.items())] + [
         "", "| derived | value |", "|---|---:|",
+        f"| launch profiled | grid {grid} threads ({waves} waves) |",
         f"| kernel duration (mean over the profiled launches) | {us:.1f} us |",
         f"| core clock (GRBM_GUI_ACTIVE / 8 XCDs / duration) | {clk:.2f} GHz |",
         f"| matrix-core busy cycles per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024) | {mfma_busy:,.0f} |",
@@ -164,9 +171,8 @@ def sq_summary(dirs):
         f"| cycles per matrix instruction issued (busy / count per SIMD) | "
         f"{mfma_busy / (vals['SQ_INSTS_VALU_MFMA_BF16'] / simds):.1f} |",
         f"| LDS instructions per wave | {vals['SQ_INSTS_LDS'] / waves:,.0f} |",
-        f"| LDS bank-conflict cycles per wave and 32-token tile (SQ_LDS_BANK_CONFLICT / 1024 "
-        f"waves / {tiles_per_unit} tiles) | "
-        f"{vals['SQ_LDS_BANK_CONFLICT'] / waves / tiles_per_unit:.1f} |",
+        f"| LDS bank-conflict cycles per wave (SQ_LDS_BANK_CONFLICT / {waves} waves) | "
+        f"{vals['SQ_LDS_BANK_CONFLICT'] / waves:,.0f} |",
         f"| wave cycles waiting on a counter (SQ_WAIT_ANY / SQ_WAVE_CYCLES) | "
         f"{vals['SQ_WAIT_ANY'] / vals['SQ_WAVE_CYCLES']:.3f} |",
     ]

@@ -70,7 +70,9 @@ def test_sq_summary_derived_figures(tmp_path):
           "SQ_ACTIVE_INST_LDS": 1.0, "SQ_INSTS_VALU": 1.0, "SQ_ACTIVE_INST_VALU": 1.0,
           "SQ_ACTIVE_INST_ANY": 1.0, "SQ_WAIT_INST_ANY": 1.0, "SQ_LDS_IDX_ACTIVE": 1.0,
           "SQ_INSTS_SALU": 1.0}
-    write_run(tmp_path / "p1", [(PARTIAL, bench.PMC_GRID, c, v, dur_ns) for c, v in v1.items()])
+    # a shorter launch of another grid (a one-part call) is not the one summarised
+    write_run(tmp_path / "p1", [(PARTIAL, bench.PMC_GRID, c, v, dur_ns) for c, v in v1.items()]
+              + [(PARTIAL, 73984, c, 1.0, dur_ns // 4) for c in v1])
     write_run(tmp_path / "p2", [(PARTIAL, bench.PMC_GRID, c, v, dur_ns) for c, v in v2.items()])
     md = bench.sq_summary([str(tmp_path / "p1"), str(tmp_path / "p2")])
     rows = dict(line.strip("|").split("|", 1) for line in md.splitlines()
@@ -86,7 +88,8 @@ def test_sq_summary_derived_figures(tmp_path):
     assert find("bf16 matrix FLOPs") == "292.0 GFLOP"
     assert find("cycles per matrix instruction") == "32.0"
     assert find("LDS instructions per wave") == "100"
-    assert find("LDS bank-conflict cycles per wave") == "3.0"
+    assert find("LDS bank-conflict cycles per wave") == "384"
+    assert find("launch profiled") == f"grid {bench.PMC_GRID} threads (1024 waves)"
     assert find("wave cycles waiting") == "0.250"
     # every counter of both passes is listed
     for c in list(v1) + list(v2):
