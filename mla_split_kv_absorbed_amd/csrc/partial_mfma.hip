@@ -443,24 +443,44 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     sh_found.u = -1;
     sh_redo = 0;
   }
-  __syncthreads();
-  const Plan pl = make_plan(pp, chunk, &sh_found, sh_scan);
-  __syncthreads();
-  if (blockIdx.x == 0 && tid == 0) *mp.ws_count = pl.nsplit_units;
   Found fd;
-  fd.u = __builtin_amdgcn_readfirstlane(sh_found.u);
-  if (fd.u < 0) return;  // grid slack beyond the plan's chunks
-  fd.tb = __builtin_amdgcn_readfirstlane(sh_found.tb);
-  fd.te = __builtin_amdgcn_readfirstlane(sh_found.te);
-  fd.slot = __builtin_amdgcn_readfirstlane(sh_found.slot);
-  fd.nsplit = __builtin_amdgcn_readfirstlane(sh_found.nsplit);
-  fd.split_idx = __builtin_amdgcn_readfirstlane(sh_found.split_idx);
+  if (pp.num_splits == 1) {
+    // One chunk per range, taken in range order: the plan is the identity
+    // and its scans are skipped (the host passes 1 when every range has the
+    // same length, where longest-first ordering changes nothing).
+    if (chunk >= pp.P * pp.B) return;  // grid slack
+    const Unit x = load_unit(pp, chunk);
+    fd.u = chunk;
+    fd.tb = 0;
+    fd.te = x.nt;
+    fd.slot = -1;
+    fd.nsplit = 1;
+    fd.split_idx = -1;
+    fd.st = x.st;
+    fd.en = x.en;
+    if (blockIdx.x == 0 && tid == 0) *mp.ws_count = 0;
+    __syncthreads();
+  } else {
+    __syncthreads();
+    const Plan pl = make_plan(pp, chunk, &sh_found, sh_scan);
+    __syncthreads();
+    if (blockIdx.x == 0 && tid == 0) *mp.ws_count = pl.nsplit_units;
+    fd.u = __builtin_amdgcn_readfirstlane(sh_found.u);
+    if (fd.u < 0) return;  // grid slack beyond the plan's chunks
+    fd.tb = __builtin_amdgcn_readfirstlane(sh_found.tb);
+    fd.te = __builtin_amdgcn_readfirstlane(sh_found.te);
+    fd.slot = __builtin_amdgcn_readfirstlane(sh_found.slot);
+    fd.nsplit = __builtin_amdgcn_readfirstlane(sh_found.nsplit);
+    fd.split_idx = __builtin_amdgcn_readfirstlane(sh_found.split_idx);
+    fd.st = __builtin_amdgcn_readfirstlane(sh_found.st);
+    fd.en = __builtin_amdgcn_readfirstlane(sh_found.en);
+  }
 
   const int p = fd.u / pp.B, b = fd.u % pp.B;
   const int t = b * S + s;
   const int Tq = pp.B * S;
-  const int st = __builtin_amdgcn_readfirstlane(sh_found.st);
-  const int en = __builtin_amdgcn_readfirstlane(sh_found.en);
+  const int st = fd.st;
+  const int en = fd.en;
   const bool unit_bad = st < 0 || en < st || (long long)en > pp.capacity;
   int vend = en;
   if (pp.mask == MLA_MASK_CAUSAL_WINDOW) vend = min(en, en - S + s + 1);
