@@ -282,7 +282,7 @@ def main():
     import torch
     from mla_split_kv_absorbed_amd import _lib as L
     from mla_split_kv_absorbed_amd import workloads as W
-    from mla_split_kv_absorbed_amd.step import DecodeStep
+    from mla_split_kv_absorbed_amd.step import DecodeStep, split_hint
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -314,9 +314,11 @@ def main():
 
     # one DCP rank's share: each part alone, a single-part call per part
     def share_args(p):
+        hint = split_hint(w.range_start[p:p + 1], w.range_end[p:p + 1], sp.S)
         a = L.partial_args(st.q_lat, st.q_rope, st.kv, st.range_start[p:p + 1].contiguous(),
                            st.range_end[p:p + 1].contiguous(), st.parts_out[p:p + 1],
                            st.parts_lse[p:p + 1], B=sp.B, S=sp.S, H=sp.H, scale=sp.scale,
+                           num_splits=hint,
                            **({"block_table": st.block_table, "block_size": sp.block_size,
                                "num_blocks": w.kv.shape[0]} if sp.block_size else
                               {"kv_seq_stride": w.kv.shape[1]}))

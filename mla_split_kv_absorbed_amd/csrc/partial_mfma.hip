@@ -444,21 +444,26 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     sh_redo = 0;
   }
   Found fd;
-  if (pp.num_splits == 1) {
-    // One chunk per range, taken in range order: the plan is the identity
-    // and its scans are skipped (the host passes 1 when every range has the
-    // same length, where longest-first ordering changes nothing).
-    if (chunk >= pp.P * pp.B) return;  // grid slack
-    const Unit x = load_unit(pp, chunk);
-    fd.u = chunk;
-    fd.tb = 0;
-    fd.te = x.nt;
-    fd.slot = -1;
-    fd.nsplit = 1;
-    fd.split_idx = -1;
+  if (pp.num_splits > 0) {
+    // An explicit count k: every range is cut into exactly k chunks (some
+    // may be empty), taken in range order, so the plan has a closed form and
+    // its scans are skipped. Chunk i of range u covers tiles
+    // [i nt / k, (i + 1) nt / k) of that range, its result goes to slot
+    // u k + i, and range u is split unit u. (The host passes k for ranges of
+    // equal length, where longest-first ordering changes nothing.)
+    const int k = pp.num_splits;
+    if (chunk >= pp.P * pp.B * k) return;  // grid slack
+    const int u = chunk / k, i = chunk % k;
+    const Unit x = load_unit(pp, u);
+    fd.u = u;
+    fd.tb = (int)((long long)i * x.nt / k);
+    fd.te = (int)((long long)(i + 1) * x.nt / k);
+    fd.slot = k > 1 ? u * k + i : -1;
+    fd.nsplit = k;
+    fd.split_idx = k > 1 ? u : -1;
     fd.st = x.st;
     fd.en = x.en;
-    if (blockIdx.x == 0 && tid == 0) *mp.ws_count = 0;
+    if (blockIdx.x == 0 && tid == 0) *mp.ws_count = k > 1 ? pp.P * pp.B : 0;
     __syncthreads();
   } else {
     __syncthreads();

@@ -17,8 +17,11 @@ from . import _lib as L
 from .workloads import D_C, D_V, Workload
 
 # workgroups one partial-attention call aims to spread over (the kernel
-# planner's target; one per compute unit)
+# planner's target; one per compute unit), keys per tile and the smallest
+# chunk the planner cuts (the library's own constants)
 TARGET_GROUPS = 256
+TILE = 32
+MIN_CHUNK_TILES = 4
 
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -31,15 +34,31 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
 
 
 def split_hint(range_start: np.ndarray, range_end: np.ndarray, S: int) -> int:
-    """Sub-split hint for mla_decode_partial from the host-side ranges: 1 (no
-    sub-splits) when every range has the same length and there are at least
-    as many (range, query) units as the kernel's target workgroup count, so
-    cutting ranges cannot improve the balance; 0 (let the kernel plan)
-    otherwise."""
-    lens = np.asarray(range_end, np.int64) - np.asarray(range_start, np.int64)
-    if lens.size and lens.min() == lens.max() and lens.size * S >= TARGET_GROUPS:
+    """Sub-split count for mla_decode_partial from the host-side ranges.
+
+    When every range has the same length and the same number of 32-key tiles,
+    the kernel's automatic plan would cut each range into the same number of
+    chunks, longest first, which for equal ranges is range order. Passing
+    that count explicitly lets the kernel skip the plan. It is 1 (no
+    sub-splits) when the (range, query) units already fill the target
+    workgroup count. Otherwise the count mirrors the plan: chunks of
+    max(4, ceil(all tiles x S / 256)) tiles. Ragged or empty ranges give 0
+    (let the kernel plan)."""
+    st = np.asarray(range_start, np.int64).ravel()
+    en = np.asarray(range_end, np.int64).ravel()
+    if not st.size:
+        return 0
+    lens = en - st
+    if lens.min() != lens.max() or lens.min() <= 0:
+        return 0
+    tiles = (en - 1) // TILE - st // TILE + 1
+    if tiles.min() != tiles.max():
+        return 0
+    nt, units = int(tiles[0]), st.size
+    if units * S >= TARGET_GROUPS:
         return 1
-    return 0
+    c = max(MIN_CHUNK_TILES, -(-units * nt * S // TARGET_GROUPS))
+    return max(1, -(-nt // c))
 
 
 class DecodeStep:
@@ -79,6 +98,7 @@ class DecodeStep:
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H, D_V), dtype=self.dt, device=dev)
 
+        explicit_splits = num_splits
         if num_splits == 0:
             num_splits = split_hint(w.range_start, w.range_end, S)
         self.num_splits = num_splits
@@ -101,7 +121,9 @@ class DecodeStep:
             self.cur_args = L.partial_args(self.q_lat, self.q_rope, self.cur_kv, self.cur_start,
                                            self.cur_end, self.cur_out, self.cur_lse,
                                            B=B, S=S, H=H, scale=sp.scale, kv_seq_stride=S,
-                                           mask=L.MLA_MASK_CAUSAL_WINDOW, num_splits=num_splits,
+                                           mask=L.MLA_MASK_CAUSAL_WINDOW,
+                                           num_splits=explicit_splits or split_hint(
+                                               np.zeros(B), np.full(B, S), S),
                                            flags=flags)
             ws = max(ws, L.mla_decode_partial_workspace_size(self.cur_args))
         self.workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)

@@ -76,17 +76,26 @@ def test_full_size_shapes_without_drawing_cache():
 
 
 def test_split_hint_policy():
-    """Host-side sub-split hint: no sub-splits only when every range has the
-    same length and the (range, query) units already fill the target
-    workgroup count."""
+    """Host-side sub-split count: for ranges of equal length it is the count
+    the kernel's automatic plan would choose (1 once the (range, query) units
+    fill the target workgroup count); ragged or empty ranges leave the plan
+    to the kernel (0)."""
     import numpy as np
     from mla_split_kv_absorbed_amd.step import TARGET_GROUPS, split_hint
     st = np.zeros((8, 32), np.int32)
     en = np.full((8, 32), 4096, np.int32)
     assert split_hint(st, en, 1) == 1                      # 256 equal units
-    assert split_hint(st[:1], en[:1], 1) == 0              # 32 units: let the kernel split
+    # 32 units of 128 tiles: chunks of max(4, 4096 / 256) = 16 tiles -> 8 per range
+    assert split_hint(st[:1], en[:1], 1) == 8
+    # 4 units of 2 tiles: chunks of at least 4 tiles -> no cut
+    assert split_hint(st[:1, :4], np.full((1, 4), 64, np.int32), 1) == 1
+    # 16 units of 100 tiles x 2 queries: chunks of 13 tiles -> 8 per range
+    assert split_hint(np.zeros(16, np.int32), np.full(16, 3200, np.int32), 2) == 8
     en2 = en.copy()
     en2[0, 0] = 100
     assert split_hint(st, en2, 1) == 0                     # ragged
+    assert split_hint(st, np.zeros_like(st), 1) == 0       # empty ranges
+    # equal lengths but a start inside a tile: different tile counts
+    assert split_hint(np.array([0, 16]), np.array([64, 80]), 1) == 0
     assert split_hint(st[:4], en[:4], 2) == 1              # 128 units x 2 queries
     assert TARGET_GROUPS == 256
