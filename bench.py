@@ -70,16 +70,29 @@ def _pmc_rows(run_dir: str, counter: str):
         return [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
 
 
+def _step_launches(rows):
+    """The partial kernel's decode-step (all parts) launches among profiled
+    rows: partial_mfma_kernel dispatches that take at least half as long as
+    the longest one. The one-part calls that bench.py times afterwards can
+    have the same grid but take a fraction of the time."""
+    rows = [r for r in rows if "partial_mfma_kernel" in r["Kernel_Name"]]
+    dur = lambda r: int(r["End_Timestamp"]) - int(r["Start_Timestamp"])  # noqa: E731
+    if not rows:
+        return rows
+    longest = max(dur(r) for r in rows)
+    return [r for r in rows if 2 * dur(r) >= longest]
+
+
 def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
     """HBM traffic per launch of the partial kernel from two rocprofv3 --pmc
     runs of the decode step (FETCH_SIZE, then WRITE_SIZE, in KiB per
     dispatch), each scaled by what the same counter reads for a plain device
     copy of known size (the copy probe)."""
     def kern_mean(d, c):
-        v = [float(r["Counter_Value"]) for r in _pmc_rows(d, c)
-             if "partial_mfma_kernel" in r["Kernel_Name"] and int(r["Grid_Size"]) == PMC_GRID]
+        v = [float(r["Counter_Value"]) for r in _step_launches(_pmc_rows(d, c))
+             if int(r["Grid_Size"]) == PMC_GRID]
         if not v:
-            raise SystemExit(f"no partial_mfma_kernel dispatch of grid {PMC_GRID} in {d}")
+            raise SystemExit(f"no partial_mfma_kernel decode-step dispatch of grid {PMC_GRID} in {d}")
         return sum(v) / len(v), len(v)
 
     def copy_mean(d, c):
@@ -111,8 +124,9 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
         "hbm_write_bytes_per_launch": int(wr),
         "hbm_bytes_per_launch": int(rd + wr),
         "commands": commands,
-        "note": f"partial_mfma_kernel dispatches with grid {PMC_GRID} (the 8-part decode-step "
-                "launch) only; the copy probe is the device copy of 512 MiB",
+        "note": f"partial_mfma_kernel decode-step dispatches (grid {PMC_GRID}, the 8-part launch; "
+                "the shorter one-part calls are excluded) only; the copy probe is the device copy "
+                "of 512 MiB",
     }
 
 
@@ -126,22 +140,16 @@ SQ_PASSES = (
 
 def sq_summary(dirs):
     """Matrix-core and LDS counters of the partial kernel's decode-step launch
-    (the partial_mfma_kernel grid with the longest mean duration: the
-    all-parts history call), from rocprofv3 --pmc runs of the SQ_PASSES
-    counter sets, as markdown."""
+    (the all-parts history call: the longest partial_mfma_kernel dispatches),
+    from rocprofv3 --pmc runs of the SQ_PASSES counter sets, as markdown."""
     import csv
     vals, durs = {}, []
     for d in dirs:
         with open(os.path.join(d, "run_counter_collection.csv")) as f:
-            rows = [r for r in csv.DictReader(f) if "partial_mfma_kernel" in r["Kernel_Name"]]
+            rows = _step_launches(list(csv.DictReader(f)))
         if not rows:
             raise SystemExit(f"no partial_mfma_kernel dispatch in {d}")
-        by_grid = {}
-        for r in rows:
-            by_grid.setdefault(int(r["Grid_Size"]), []).append(
-                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        grid = max(by_grid, key=lambda g: sum(by_grid[g]) / len(by_grid[g]))
-        rows = [r for r in rows if int(r["Grid_Size"]) == grid]
+        grid = int(rows[0]["Grid_Size"])
         per = {}
         for r in rows:
             per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))

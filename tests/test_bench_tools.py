@@ -33,10 +33,12 @@ def test_pmc_summary_scales_by_the_copy_probe(tmp_path):
     # the copy probe reads half its bytes in FETCH_SIZE units (factor 2), writes all (factor 1)
     write_run(tmp_path / "cf", [(COPY, 1 << 20, "FETCH_SIZE", n_copy / 2048, 10)] * 3)
     write_run(tmp_path / "cw", [(COPY, 1 << 20, "WRITE_SIZE", n_copy / 1024, 10)] * 3)
-    # two decode-step launches (the counted grid) and one one-part launch (ignored)
-    write_run(tmp_path / "kf", [(PARTIAL, bench.PMC_GRID, "FETCH_SIZE", 500.0, 10),
-                                (PARTIAL, bench.PMC_GRID, "FETCH_SIZE", 700.0, 10),
-                                (PARTIAL, 73984, "FETCH_SIZE", 1e9, 10)])
+    # two decode-step launches (the counted grid), one one-part launch of another
+    # grid and one of the same grid but a quarter of the duration (both ignored)
+    write_run(tmp_path / "kf", [(PARTIAL, bench.PMC_GRID, "FETCH_SIZE", 500.0, 100),
+                                (PARTIAL, bench.PMC_GRID, "FETCH_SIZE", 700.0, 100),
+                                (PARTIAL, 73984, "FETCH_SIZE", 1e9, 10),
+                                (PARTIAL, bench.PMC_GRID, "FETCH_SIZE", 1e9, 25)])
     write_run(tmp_path / "kw", [(PARTIAL, bench.PMC_GRID, "WRITE_SIZE", 40.0, 10)])
     res = bench.pmc_summary(str(tmp_path / "kf"), str(tmp_path / "kw"), str(tmp_path / "cf"),
                             str(tmp_path / "cw"), ["cmd"])
@@ -70,9 +72,10 @@ def test_sq_summary_derived_figures(tmp_path):
           "SQ_ACTIVE_INST_LDS": 1.0, "SQ_INSTS_VALU": 1.0, "SQ_ACTIVE_INST_VALU": 1.0,
           "SQ_ACTIVE_INST_ANY": 1.0, "SQ_WAIT_INST_ANY": 1.0, "SQ_LDS_IDX_ACTIVE": 1.0,
           "SQ_INSTS_SALU": 1.0}
-    # a shorter launch of another grid (a one-part call) is not the one summarised
+    # shorter launches (one-part calls, of another grid or the same one) are not summarised
     write_run(tmp_path / "p1", [(PARTIAL, bench.PMC_GRID, c, v, dur_ns) for c, v in v1.items()]
-              + [(PARTIAL, 73984, c, 1.0, dur_ns // 4) for c in v1])
+              + [(PARTIAL, 73984, c, 1.0, dur_ns // 4) for c in v1]
+              + [(PARTIAL, bench.PMC_GRID, c, 1.0, dur_ns // 4) for c in v1])
     write_run(tmp_path / "p2", [(PARTIAL, bench.PMC_GRID, c, v, dur_ns) for c, v in v2.items()])
     md = bench.sq_summary([str(tmp_path / "p1"), str(tmp_path / "p2")])
     rows = dict(line.strip("|").split("|", 1) for line in md.splitlines()
