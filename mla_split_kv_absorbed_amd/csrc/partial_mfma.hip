@@ -47,8 +47,10 @@
 // are spread over the score product.
 //
 // Ranges that need splitting (few sequences, long ranges) are cut into
-// chunks; chunk results go to a fp32 workspace and a second kernel merges
-// them by LSE in a fixed order.
+// chunks; chunk results go to a workspace (outputs in the output type, LSEs
+// in fp32) and a second kernel merges them by LSE in a fixed order. The
+// chunks come from an in-kernel plan, or, with an explicit split count, from
+// a closed form that needs no plan.
 #include "common.h"
 #include "kernels.h"
 
