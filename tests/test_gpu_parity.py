@@ -251,7 +251,13 @@ def test_partial_full_size_every_row(wid):
     assert np.all(d_l <= allow)
 
 
-def test_partial_edge_ranges():
+# (flags, num_splits): the matrix kernel with its in-kernel plan (0) and with
+# explicit split counts (1, 3: the closed-form chunks), and the plain kernel
+EDGE_PATHS = [(0, 0), (0, 1), (0, 3), (L.MLA_FLAG_FORCE_SIMPLE, 0)]
+
+
+@pytest.mark.parametrize("flags,splits", EDGE_PATHS)
+def test_partial_edge_ranges(flags, splits):
     """Empty ranges, single-key ranges, ranges starting mid-block, a zero
     length sequence and unaligned starts."""
     sp = W.spec(2, B=4, lengths=("fixed", 300), parts=4)
@@ -261,12 +267,12 @@ def test_partial_edge_ranges():
                   dtype=np.int32)
     re = np.array([[0, 37, 1, 299], [10, 37, 1, 300], [10, 300, 2, 300], [300, 300, 300, 300]],
                   dtype=np.int32)
-    for flags in (0, L.MLA_FLAG_FORCE_SIMPLE):
-        st = run_partial(w, qs, flags=flags, ranges=(rs, re))
-        check_partial(w, st, qs, ranges=(rs, re))
+    st = run_partial(w, qs, flags=flags, num_splits=splits, ranges=(rs, re))
+    check_partial(w, st, qs, ranges=(rs, re))
 
 
-def test_partial_invalid_metadata_is_contained():
+@pytest.mark.parametrize("flags,splits", EDGE_PATHS)
+def test_partial_invalid_metadata_is_contained(flags, splits):
     """A range past the table or a bad block id poisons only its own
     (part, sequence) with NaN; nothing is read out of bounds."""
     sp = W.spec(2, B=3, lengths=("fixed", 256), parts=2)
@@ -278,16 +284,15 @@ def test_partial_invalid_metadata_is_contained():
     re[0, 2] = 10              # start > end
     bt = w.block_table.copy()
     bt[1, 1] = 1 << 30         # a referenced block id out of range
-    for flags in (0, L.MLA_FLAG_FORCE_SIMPLE):
-        st = run_partial(w, qs, flags=flags, ranges=(rs, re), block_table=bt)
-        out, lse = f64(st.parts_out), f64(st.parts_lse)
-        bad = {(1, 0), (0, 2), (0, 1)}
-        for p in range(2):
-            for b in range(3):
-                if (p, b) in bad:
-                    assert np.all(np.isnan(out[p, b])) and np.all(np.isnan(lse[p, b])), (p, b)
-                else:
-                    assert np.all(np.isfinite(out[p, b])) and np.all(np.isfinite(lse[p, b]))
+    st = run_partial(w, qs, flags=flags, num_splits=splits, ranges=(rs, re), block_table=bt)
+    out, lse = f64(st.parts_out), f64(st.parts_lse)
+    bad = {(1, 0), (0, 2), (0, 1)}
+    for p in range(2):
+        for b in range(3):
+            if (p, b) in bad:
+                assert np.all(np.isnan(out[p, b])) and np.all(np.isnan(lse[p, b])), (p, b)
+            else:
+                assert np.all(np.isfinite(out[p, b])) and np.all(np.isfinite(lse[p, b]))
 
 
 def test_partial_deterministic_and_permutation_invariant():
