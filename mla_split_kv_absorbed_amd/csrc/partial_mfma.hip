@@ -446,6 +446,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     sh_redo = 0;
   }
   Found fd;
+  bool first;  // this piece is the first of its range
   if (pp.num_splits > 0) {
     // An explicit count k: every range is cut into exactly k chunks (some
     // may be empty), taken in range order, so the plan has a closed form and
@@ -465,10 +466,10 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     fd.split_idx = k > 1 ? u : -1;
     fd.st = x.st;
     fd.en = x.en;
+    // a range shorter than k tiles has several pieces that start at tile 0:
+    // piece 0 alone is the first
+    first = i == 0;
     if (blockIdx.x == 0 && tid == 0) *mp.ws_count = k > 1 ? pp.P * pp.B : 0;
-    // piece 0 records where the range's k results live (a range shorter than
-    // k tiles has several pieces that start at tile 0; only piece 0 writes)
-    if (k > 1 && i == 0 && s == 0 && tid == 0) mp.ws_desc[u] = intx4{u, u * k, k, 0};
     __syncthreads();
   } else {
     __syncthreads();
@@ -484,10 +485,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     fd.split_idx = __builtin_amdgcn_readfirstlane(sh_found.split_idx);
     fd.st = __builtin_amdgcn_readfirstlane(sh_found.st);
     fd.en = __builtin_amdgcn_readfirstlane(sh_found.en);
-    // chunk 0 of a split range records where its chunks' results live (the
-    // plan gives every chunk at least one tile, so only chunk 0 starts at 0)
-    if (fd.split_idx >= 0 && fd.tb == 0 && s == 0 && tid == 0)
-      mp.ws_desc[fd.split_idx] = intx4{fd.u, fd.slot, fd.nsplit, 0};
+    // the plan gives every chunk at least one tile: only chunk 0 starts at 0
+    first = fd.tb == 0;
   }
 
   const int p = fd.u / pp.B, b = fd.u % pp.B;
@@ -498,6 +497,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const bool unit_bad = st < 0 || en < st || (long long)en > pp.capacity;
   int vend = en;
   if (pp.mask == MLA_MASK_CAUSAL_WINDOW) vend = min(en, en - S + s + 1);
+  // the first piece of a split range records where its pieces' results live
+  if (fd.split_idx >= 0 && first && s == 0 && tid == 0)
+    mp.ws_desc[fd.split_idx] = intx4{fd.u, fd.slot, fd.nsplit, 0};
 
   // ---- per-lane constants -------------------------------------------------
   const int hi = lane >> 5;          // 0/1: which half of a 16-wide k step
