@@ -226,6 +226,13 @@ def cpu_baseline(w, budget_s: float = 15.0):
                       f"{total_pairs}/{done}"}
 
 
+def spread(xs):
+    """Median, 10th and 90th percentile of a list of durations (us)."""
+    q = np.percentile(np.asarray(xs, np.float64), [50, 10, 90])
+    return {"median": round(float(q[0]), 2), "p10": round(float(q[1]), 2),
+            "p90": round(float(q[2]), 2), "n": len(xs)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -344,13 +351,10 @@ def main():
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
-    print("[bench] timing", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e_start = torch.cuda.Event(enable_timing=True)
-    e_end = torch.cuda.Event(enable_timing=True)
-    e_start.record(stream)
-    for i in range(args.steps):
+
+    # one decode step on cache copy i % copies, the partial call bracketed by
+    # the events ev[i]
+    def one_step(i):
         st = sts[i % copies]
         if st.absorb:
             L.mla_q_absorb(st.q_nope, st.w_uk, st.q_lat, stream)
@@ -372,11 +376,32 @@ def main():
                                   local_lse=st.cur_lse if sp.current else None, stream=stream)
                 x = st.lat
             L.mla_vup(x, st.w_uv, st.out, stream)
+
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e_start = torch.cuda.Event(enable_timing=True)
+    e_end = torch.cuda.Event(enable_timing=True)
+    e_start.record(stream)
+    for i in range(args.steps):
+        one_step(i)
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e_start.elapsed_time(e_end) / args.steps
-    part_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    part_launch = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    part_ms = float(np.mean(part_launch)) * 1e-3
+
+    # the spread of single steps, from a second pass with an event between
+    # consecutive steps (outside the timed region: the events are the only
+    # difference)
+    sev_step = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    sev_step[0].record(stream)
+    for i in range(args.steps):
+        one_step(i)
+        sev_step[i + 1].record(stream)
+    torch.cuda.synchronize()
+    step_us = [sev_step[i].elapsed_time(sev_step[i + 1]) * 1e3 for i in range(args.steps)]
 
     # each rank's share timed alone, the parts called in turn (each call
     # meets its part's keys cold: the other parts' keys came in between)
@@ -444,6 +469,8 @@ def main():
                      "traffic": traffic, "bytes_per_launch": part_bytes,
                      "avg_launch_us": round(part_ms * 1e3, 2),
                      "mfma_tflops": round(work["attn_flops"] / (part_ms * 1e-3) / 1e12, 1)},
+        "step_us_spread": spread(step_us),
+        "partial_launch_us_spread": spread(part_launch),
         "one_rank_share_us": round(share_us, 2),
         "one_rank_share_per_part_us": [round(x, 2) for x in share_per_part],
         "kv_cache_copies": copies,

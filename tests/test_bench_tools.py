@@ -106,3 +106,10 @@ def test_sq_passes_fit_one_run_each():
         assert sum(n.startswith("SQ_") for n in names) <= 8
         assert sum(n.startswith("GRBM_") for n in names) <= 2
         assert len(set(names)) == len(names)
+
+
+def test_spread_percentiles():
+    """Median and 10th / 90th percentiles of step durations (linear interpolation)."""
+    xs = [float(v) for v in range(1, 102)]  # 1 .. 101
+    r = bench.spread(xs[::-1])
+    assert r == {"median": 51.0, "p10": 11.0, "p90": 91.0, "n": 101}
