@@ -386,6 +386,7 @@ def main():
     for i in range(args.steps):
         one_step(i)
     e_end.record(stream)
+    enqueue_s = time.perf_counter() - t0
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = e_start.elapsed_time(e_end) / args.steps
@@ -475,6 +476,7 @@ def main():
         "one_rank_share_per_part_us": [round(x, 2) for x in share_per_part],
         "kv_cache_copies": copies,
         "wall_s": round(wall, 3),
+        "host_enqueue_s": round(enqueue_s, 4),
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle sample)", file=sys.stderr, flush=True)

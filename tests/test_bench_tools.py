@@ -113,3 +113,4 @@ def test_spread_percentiles():
     xs = [float(v) for v in range(1, 102)]  # 1 .. 101
     r = bench.spread(xs[::-1])
     assert r == {"median": 51.0, "p10": 11.0, "p90": 91.0, "n": 101}
+
