@@ -115,7 +115,9 @@ enum {
  *   the results of sub-ranges (in out_dtype, with fp32 LSEs) until they are
  *   merged inside the call.
  * num_splits: 0 = automatic; otherwise each (part, sequence) range is cut
- *   into at most this many sub-ranges that are merged inside the call. With
+ *   into at most this many sub-ranges that are merged inside the call (the
+ *   sub-ranges of one range run on one XCD when the range count P x B is a
+ *   multiple of 8). With
  *   1 every range is one unit of work, dispatched in range order (best when
  *   the ranges have equal lengths and there are at least a few hundred of
  *   them; the automatic plan dispatches the longest first).

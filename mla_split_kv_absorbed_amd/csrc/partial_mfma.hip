@@ -449,14 +449,27 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   bool first;  // this piece is the first of its range
   if (pp.num_splits > 0) {
     // An explicit count k: every range is cut into exactly k chunks (some
-    // may be empty), taken in range order, so the plan has a closed form and
-    // its scans are skipped. Chunk i of range u covers tiles
-    // [i nt / k, (i + 1) nt / k) of that range, its result goes to slot
-    // u k + i, and range u is split unit u. (The host passes k for ranges of
-    // equal length, where longest-first ordering changes nothing.)
+    // may be empty), so the plan has a closed form and its scans are
+    // skipped. Chunk i of range u covers tiles [i nt / k, (i + 1) nt / k) of
+    // that range, its result goes to slot u k + i, and range u is split
+    // unit u. (The host passes k for ranges of equal length, where
+    // longest-first ordering changes nothing.) Chunk c runs on XCD c mod 8;
+    // when the range count is a multiple of 8, the k chunks of a range all
+    // get the same residue (c = x + 8 (k (u div 8) + i), x = u mod 8), so the
+    // rows of Q they share are fetched into one L2. Otherwise chunks follow
+    // range order (c = u k + i). With k = 1 both orders are the identity.
     const int k = pp.num_splits;
-    if (chunk >= pp.P * pp.B * k) return;  // grid slack
-    const int u = chunk / k, i = chunk % k;
+    const int nunits = pp.P * pp.B;
+    if (chunk >= nunits * k) return;  // grid slack
+    int u, i;
+    if ((nunits & 7) == 0) {
+      const int pos = chunk >> 3;  // position among the chunks of XCD chunk & 7
+      u = (chunk & 7) + 8 * (pos / k);
+      i = pos % k;
+    } else {
+      u = chunk / k;
+      i = chunk % k;
+    }
     const Unit x = load_unit(pp, u);
     fd.u = u;
     fd.tb = (int)((long long)i * x.nt / k);
