@@ -265,9 +265,12 @@ def main():
         return
     if args.pmc_summary:
         dirs = args.pmc_summary
+        # the commands name the output folders relative to the repository
+        rel = [os.path.relpath(os.path.abspath(d), ROOT)
+               if os.path.abspath(d).startswith(ROOT + os.sep) else d for d in dirs]
         cmds = [f"rocprofv3 --pmc {c} --output-format csv -d {d} -o run -- python3 bench.py "
                 + ("--copy-probe" if i >= 2 else "--steps 2 --warmup 1 --no-cpu-baseline")
-                for i, (c, d) in enumerate(zip(("FETCH_SIZE", "WRITE_SIZE") * 2, dirs))]
+                for i, (c, d) in enumerate(zip(("FETCH_SIZE", "WRITE_SIZE") * 2, rel))]
         res = pmc_summary(*dirs, cmds)
         with open(PMC_FILE, "w") as f:
             json.dump(res, f, indent=1)
