@@ -215,6 +215,24 @@ def test_partial_split_count_invariance(splits):
     check_partial(w, st, qs)
 
 
+@pytest.mark.parametrize("B,lengths,splits", [
+    (8, ("fixed", 700), 3),           # 22 tiles per range, uneven pieces
+    (8, ("uniform", 40, 2000), 8),    # ragged: some ranges shorter than 8 tiles
+    (16, ("uniform", 100, 1200), 5),  # two ranges per XCD residue
+])
+def test_partial_split_xcd_grouped(B, lengths, splits):
+    """With an explicit split count and a range count that is a multiple of
+    8, the pieces of a range run on one XCD (a different chunk order); the
+    merged result still matches the oracle, empty pieces included."""
+    sp = W.spec(1, B=B, lengths=lengths)
+    say(f"[xcd-grouped] B={B} lengths={lengths} splits={splits}")
+    w = W.make_workload(sp)
+    assert (sp.parts * B) % 8 == 0
+    qs = oracle_qlat(w)
+    st = run_partial(w, qs, num_splits=splits)
+    check_partial(w, st, qs)
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
 def test_partial_full_size_every_row(wid):
     """Every (part, query, head) row of a full-size workload is written,
