@@ -293,8 +293,36 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
   Plan pl;
   const long long want_groups = kTargetGroups;
   const long long cw = ((long long)total * pp.S + want_groups - 1) / want_groups;
-  pl.chunk_tiles = (int)max((long long)kMinChunkTiles, cw);
-  const int c = pl.chunk_tiles;
+  int c = (int)max((long long)kMinChunkTiles, cw);
+  // Chunks of c tiles give at most U + G / S chunks (G = kTargetGroups
+  // workgroups, S per chunk). Between one and two rounds of G workgroups,
+  // the second round is short and leaves most compute units idle at the
+  // end; a smaller chunk c1 that makes about two full rounds (U S / 2 for
+  // the rounding of each range, hence 2 S T / (4 G - U S)) is taken when
+  // its chunks still fit in two rounds. c1 >= S T / (2 G) keeps the chunk
+  // count within the grid bound max(U + G / S, 2 G / S) + 1, and split slots
+  // within 2 G / S.
+  {
+    const long long su = (long long)pp.S * U;
+    if (4LL * kTargetGroups > su) {
+      long long c1 = (2LL * pp.S * total + 4LL * kTargetGroups - su - 1) / (4LL * kTargetGroups - su);
+      c1 = max(c1, ((long long)total * pp.S + 2LL * kTargetGroups - 1) / (2LL * kTargetGroups));
+      c1 = max(c1, (long long)kMinChunkTiles);
+      if (c1 < c) {
+        int nv[2] = {0, 0}, nb[2], ntot[2];
+        for (int i = 0; i < u1 - u0; ++i) {
+          const int nt = unit_at(i).nt;
+          nv[0] += unit_chunks(nt, c, 0);
+          nv[1] += unit_chunks(nt, (int)c1, 0);
+        }
+        block_excl_scan<2>(nv, sh, nb, ntot);
+        if ((long long)pp.S * ntot[0] > kTargetGroups &&
+            (long long)pp.S * ntot[1] <= 2LL * kTargetGroups)
+          c = (int)c1;
+      }
+    }
+  }
+  pl.chunk_tiles = c;
   // per bucket chunk counts of this thread, plus all chunks, split slots and
   // split units
   int mv[kBuckets + 3];
@@ -1114,7 +1142,9 @@ bool mfma_path_supported(int dtype, int H, int block_size) {
 size_t mfma_max_chunks(int B, int S, int P, int hint) {
   const size_t U = (size_t)P * B;
   if (hint > 0) return U * hint;
-  return U + (kTargetGroups + S - 1) / S + 1;
+  // the plan's chunk size gives at most U + G / S chunks, or 2 G / S when it
+  // takes the smaller size that fills two rounds
+  return std::max(U + (kTargetGroups + S - 1) / S, (size_t)(2 * kTargetGroups + S - 1) / S) + 1;
 }
 
 size_t mfma_workspace_bytes(int B, int S, int H, int P, int hint, int out_dtype) {

@@ -42,8 +42,10 @@ def split_hint(range_start: np.ndarray, range_end: np.ndarray, S: int) -> int:
     that count explicitly lets the kernel skip the plan. It is 1 (no
     sub-splits) when the (range, query) units already fill the target
     workgroup count. Otherwise the count mirrors the plan: chunks of
-    max(4, ceil(all tiles x S / 256)) tiles. Ragged or empty ranges give 0
-    (let the kernel plan)."""
+    c = max(4, ceil(all tiles x S / 256)) tiles, or, when those make between
+    one and two rounds of 256 workgroups, the smaller chunk that fills two
+    rounds if its chunks fit in them. Ragged or empty ranges give 0 (let the
+    kernel plan)."""
     st = np.asarray(range_start, np.int64).ravel()
     en = np.asarray(range_end, np.int64).ravel()
     if not st.size:
@@ -57,7 +59,12 @@ def split_hint(range_start: np.ndarray, range_end: np.ndarray, S: int) -> int:
     nt, units = int(tiles[0]), st.size
     if units * S >= TARGET_GROUPS:
         return 1
-    c = max(MIN_CHUNK_TILES, -(-units * nt * S // TARGET_GROUPS))
+    G, total = TARGET_GROUPS, units * nt
+    c = max(MIN_CHUNK_TILES, -(-total * S // G))
+    if 4 * G > S * units:
+        c1 = max(MIN_CHUNK_TILES, -(-2 * S * total // (4 * G - S * units)), -(-total * S // (2 * G)))
+        if c1 < c and S * units * -(-nt // c) > G and S * units * -(-nt // c1) <= 2 * G:
+            c = c1
     return max(1, -(-nt // c))
 
 

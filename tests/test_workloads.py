@@ -98,4 +98,14 @@ def test_split_hint_policy():
     # equal lengths but a start inside a tile: different tile counts
     assert split_hint(np.array([0, 16]), np.array([64, 80]), 1) == 0
     assert split_hint(st[:4], en[:4], 2) == 1              # 128 units x 2 queries
+    # 40 units of 50 tiles: chunks of 8 tiles make 280 workgroups (one round
+    # and a short one); chunks of max(4, ceil(2 x 2000 / (1024 - 40)), ceil(2000 / 512)) = 5
+    # make 400, two rounds -> 10 per range
+    assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 1) == 10
+    # x 4 queries: chunks of 32 tiles make 320 workgroups; chunks of
+    # max(ceil(16000 / 864), ceil(8000 / 512)) = 19 make 480 -> 3 per range
+    assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 4) == 3
+    # x 8 queries: c = 63 makes 320 workgroups, but c1 = 46 would make 640,
+    # more than two rounds: 63 is kept -> 1 per range
+    assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 8) == 1
     assert TARGET_GROUPS == 256
