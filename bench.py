@@ -31,6 +31,10 @@ MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 KERNEL_SRCS = [os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", f)
                for f in ("partial_mfma.hip", "common.h", "kernels.h")]
 PMC_FILE = os.path.join(ROOT, "profiles", "partial_mfma_kernel_pmc.json")
+# how the timed decode step is built (the full-size parity tests build theirs
+# the same way): a single part's sub-ranges are cut on the host and merged by
+# the fused combine + V-up
+BENCH_STEP_OPTS = {"host_subranges": True}
 
 
 def kernel_hash(srcs=None) -> str:
@@ -326,15 +330,18 @@ def main():
     kv_bytes = w.kv.nbytes
     copies = args.copies or (1 if kv_bytes >= MALL_BYTES * 2 or kv_bytes < 16 << 20
                              else -(-(2 * MALL_BYTES) // kv_bytes) + 1)
-    sts = [DecodeStep(w, device="cuda:0") for _ in range(copies)]
+    sts = [DecodeStep(w, device="cuda:0", **BENCH_STEP_OPTS) for _ in range(copies)]
     st = sts[0]
     stream = torch.cuda.current_stream()
 
     # one DCP rank's share: each part alone, a single-part call per part
     def share_args(p):
+        # the workload's own range of part p (the step's device ranges may be
+        # its host-cut sub-ranges)
         hint = split_hint(w.range_start[p:p + 1], w.range_end[p:p + 1], sp.S)
-        a = L.partial_args(st.q_lat, st.q_rope, st.kv, st.range_start[p:p + 1].contiguous(),
-                           st.range_end[p:p + 1].contiguous(), st.parts_out[p:p + 1],
+        rs = torch.from_numpy(np.ascontiguousarray(w.range_start[p:p + 1])).to("cuda:0")
+        re_ = torch.from_numpy(np.ascontiguousarray(w.range_end[p:p + 1])).to("cuda:0")
+        a = L.partial_args(st.q_lat, st.q_rope, st.kv, rs, re_, st.parts_out[p:p + 1],
                            st.parts_lse[p:p + 1], B=sp.B, S=sp.S, H=sp.H, scale=sp.scale,
                            num_splits=hint,
                            **({"block_table": st.block_table, "block_size": sp.block_size,
@@ -343,7 +350,7 @@ def main():
         ws_ = torch.empty(max(1, L.mla_decode_partial_workspace_size(a)), dtype=torch.uint8,
                           device="cuda:0")
         a.workspace, a.workspace_bytes = ws_.data_ptr(), ws_.numel()
-        return a, ws_
+        return a, (ws_, rs, re_)  # kept alive with the arguments
     shares = [share_args(p) for p in range(sp.parts)]
 
     print(f"[bench] warmup ({copies} cache cop{'y' if copies == 1 else 'ies'})",

@@ -68,12 +68,40 @@ def split_hint(range_start: np.ndarray, range_end: np.ndarray, S: int) -> int:
     return max(1, -(-nt // c))
 
 
+def cut_ranges(range_start: np.ndarray, range_end: np.ndarray, k: int):
+    """Each range [start, end) cut into k pieces on 32-key tile boundaries:
+    piece i takes tiles [i nt / k, (i + 1) nt / k) of the range's nt tiles
+    (the kernel's own cut), clipped to the range. Returns [k][n] starts and
+    ends; a piece with no tile is empty."""
+    st = np.asarray(range_start, np.int64).ravel()
+    en = np.asarray(range_end, np.int64).ravel()
+    out_st = np.zeros((k, st.size), np.int32)
+    out_en = np.zeros((k, st.size), np.int32)
+    for j, (a, e) in enumerate(zip(st, en)):
+        if e <= a:
+            out_st[:, j] = out_en[:, j] = a
+            continue
+        t0, nt = a // TILE, (e - 1) // TILE - a // TILE + 1
+        for i in range(k):
+            lo, hi = i * nt // k, (i + 1) * nt // k
+            ps = a if lo == 0 else (t0 + lo) * TILE
+            pe = min(e, (t0 + hi) * TILE) if hi > lo else ps
+            out_st[i, j], out_en[i, j] = ps, max(ps, pe)
+    return out_st, out_en
+
+
 class DecodeStep:
     """Device-resident inputs, outputs and workspace of one decode step."""
 
     def __init__(self, w: Workload, device="cuda", part_lse_dtype: Optional[str] = None,
                  num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None,
-                 side_stream: bool = False, fused_tail: bool = True, keep_latent: bool = False):
+                 side_stream: bool = False, fused_tail: bool = True, keep_latent: bool = False,
+                 host_subranges: bool = False):
+        """host_subranges: a single part without a current chunk, whose
+        ranges the partial call would cut into k > 1 sub-ranges (equal ranges,
+        bf16 / fp16), is instead cut on the host (cut_ranges) and passed as k
+        parts, merged by the fused combine + V-up; the partial then runs
+        without its own merge launch."""
         sp = w.spec
         self.w = w
         self.dev = torch.device(device)
@@ -93,8 +121,16 @@ class DecodeStep:
         self.kv = to_device(w.kv, dt, dev)
         self.block_table = (torch.from_numpy(w.block_table).to(dev)
                             if w.block_table is not None else None)
-        self.range_start = torch.from_numpy(w.range_start).to(dev)
-        self.range_end = torch.from_numpy(w.range_end).to(dev)
+        rs, re_ = w.range_start, w.range_end
+        self.host_cut = 1
+        if (host_subranges and P == 1 and not sp.current and num_splits == 0
+                and dt in ("bf16", "f16")):
+            k = split_hint(rs, re_, S)
+            if k > 1:
+                rs, re_ = cut_ranges(rs, re_, k)
+                self.host_cut, P, self.P, num_splits = k, k, k, 1
+        self.range_start = torch.from_numpy(np.ascontiguousarray(rs)).to(dev)
+        self.range_end = torch.from_numpy(np.ascontiguousarray(re_)).to(dev)
         self.q_lat = torch.empty((T, H, D_C), dtype=self.dt, device=dev)
         self.absorb = q_lat_in is None
         if q_lat_in is not None:

@@ -15,6 +15,8 @@ import numpy as np
 import pytest
 import torch
 
+import bench
+
 import oracle.mla_oracle as mo
 from mla_split_kv_absorbed_amd import _lib as L
 from mla_split_kv_absorbed_amd import workloads as W
@@ -99,6 +101,23 @@ def test_step_small(name):
         check_step(w, st32, list(range(sp.B)), heads)
 
 
+def test_step_host_subranges():
+    """A single part cut into sub-ranges on the host and passed as parts
+    (merged by the fused combine + V-up) matches the oracle, ragged last tile
+    included, and the step built the default way."""
+    sp = W.spec(1, B=4, lengths=("fixed", 1000))
+    w = W.make_workload(sp)
+    st = DecodeStep(w, host_subranges=True)
+    assert st.host_cut == 8 and st.P == 8 and st.fused_tail
+    st.run()
+    ref = DecodeStep(w)
+    ref.run()
+    torch.cuda.synchronize()
+    check_step(w, st, list(range(sp.B)), list(range(0, sp.H, 9)))
+    otol, _ = TOL[sp.dtype]
+    assert (st.out.float() - ref.out.float()).abs().max().item() <= otol
+
+
 FULL = [1, 2, 3, 4]
 
 
@@ -109,8 +128,8 @@ def test_step_full_size_sampled(wid):
     sp = W.SPECS[wid]
     say(f"[full] {sp.name}: generating")
     w = W.make_workload(sp)
-    st = DecodeStep(w)
-    say(f"[full] {sp.name}: running")
+    st = DecodeStep(w, **bench.BENCH_STEP_OPTS)
+    say(f"[full] {sp.name}: running (host sub-ranges: {st.host_cut})")
     st.run()
     torch.cuda.synchronize()
     r = np.random.Generator(np.random.PCG64(7 + wid))

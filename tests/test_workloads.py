@@ -109,3 +109,41 @@ def test_split_hint_policy():
     # more than two rounds: 63 is kept -> 1 per range
     assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 8) == 1
     assert TARGET_GROUPS == 256
+
+
+def test_cut_ranges_tiles_each_range_exactly():
+    """Host sub-ranges: k pieces per range, in order, disjoint, covering the
+    range, with inner boundaries on 32-key tiles, piece i holding tiles
+    [i nt / k, (i + 1) nt / k); empty ranges give empty pieces."""
+    import numpy as np
+    from mla_split_kv_absorbed_amd.step import cut_ranges
+    rng = np.random.default_rng(5)
+    st = rng.integers(0, 300, 64)
+    en = st + rng.integers(0, 900, 64)
+    st[:2], en[:2] = 100, 100          # empty ranges
+    st[2], en[2] = 0, 4096             # aligned
+    for k in (1, 2, 3, 8):
+        ps, pe = cut_ranges(st, en, k)
+        assert ps.shape == (k, 64) and pe.shape == (k, 64)
+        for j in range(64):
+            a, e = int(st[j]), int(en[j])
+            if e <= a:
+                assert np.all(ps[:, j] == a) and np.all(pe[:, j] == a)
+                continue
+            nt = (e - 1) // 32 - a // 32 + 1
+            covered = []
+            for i in range(k):
+                assert ps[i, j] <= pe[i, j]
+                tiles = (i + 1) * nt // k - i * nt // k
+                if tiles == 0:
+                    assert ps[i, j] == pe[i, j]
+                    continue
+                covered.append((int(ps[i, j]), int(pe[i, j])))
+                first_tile = ps[i, j] // 32 if ps[i, j] != a else a // 32
+                assert (pe[i, j] - 1) // 32 - first_tile + 1 == tiles
+                if ps[i, j] != a:
+                    assert ps[i, j] % 32 == 0
+            # the non-empty pieces tile [a, e) in order
+            assert covered[0][0] == a and covered[-1][1] == e
+            for (s0, e0), (s1, e1) in zip(covered, covered[1:]):
+                assert e0 == s1
