@@ -54,3 +54,21 @@ def test_two_round_size_on_a_ragged_batch():
     c = plan_chunk_tiles(nts, 1)
     assert c == max(MIN_CHUNK, -(-2 * 7720 // (1024 - 256)), -(-7720 // 512))   # 21
     assert G < chunks(nts, 31).sum() and chunks(nts, c).sum() <= 2 * G
+
+
+def test_split_hint_matches_the_plan_on_equal_ranges():
+    """For equal ranges the host's split_hint gives the chunk count per range
+    that the plan's rule gives (or 1 once the ranges alone fill the target)."""
+    from mla_split_kv_absorbed_amd.step import TILE, split_hint
+    rng = np.random.default_rng(11)
+    for _ in range(3000):
+        U = int(rng.integers(1, 600))
+        S = int(rng.integers(1, 5))
+        L = int(rng.integers(1, 40000))
+        nt = (L - 1) // TILE + 1
+        hint = split_hint(np.zeros(U, np.int32), np.full(U, L, np.int32), S)
+        if U * S >= G:
+            assert hint == 1
+        else:
+            c = plan_chunk_tiles(np.full(U, nt), S)
+            assert hint == max(1, -(-nt // c)), (U, S, L)
