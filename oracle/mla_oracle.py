@@ -182,15 +182,12 @@ def latent_partial(q_lat: np.ndarray, q_rope: np.ndarray, rows: np.ndarray,
     S, H, d_c = q_lat.shape
     keys = rows[start:end]
     n = keys.shape[0]
-    vis = causal_window_visible(n, S) if causal else None
-    o = np.zeros((S, H, d_c))
-    l = np.full((S, H), NEG_INF)
-    for h in range(H):
-        q = np.concatenate([q_lat[:, h], q_rope[:, h]], axis=1)
-        oh, lh = attend(q, keys, keys[:, :d_c], scale, vis)
-        o[:, h] = oh
-        l[:, h] = lh
-    return o, l
+    # every (query, head) pair is one query row of the same key set: the S*H
+    # rows go through attend together (each row's softmax is its own)
+    q = np.concatenate([q_lat, q_rope], axis=2).reshape(S * H, -1)
+    vis = np.repeat(causal_window_visible(n, S), H, axis=0) if causal else None
+    o, l = attend(q, keys, keys[:, :d_c], scale, vis)
+    return o.reshape(S, H, d_c), l.reshape(S, H)
 
 
 def lse_combine(outs: np.ndarray, lses: np.ndarray):
