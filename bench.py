@@ -304,7 +304,7 @@ def main():
     import torch
     from mla_split_kv_absorbed_amd import _lib as L
     from mla_split_kv_absorbed_amd import workloads as W
-    from mla_split_kv_absorbed_amd.step import DecodeStep, split_hint
+    from mla_split_kv_absorbed_amd.step import DecodeStep
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -338,15 +338,16 @@ def main():
     def share_args(p):
         # the workload's own range of part p (the step's device ranges may be
         # its host-cut sub-ranges)
-        hint = split_hint(w.range_start[p:p + 1], w.range_end[p:p + 1], sp.S)
         rs = torch.from_numpy(np.ascontiguousarray(w.range_start[p:p + 1])).to("cuda:0")
         re_ = torch.from_numpy(np.ascontiguousarray(w.range_end[p:p + 1])).to("cuda:0")
         a = L.partial_args(st.q_lat, st.q_rope, st.kv, rs, re_, st.parts_out[p:p + 1],
                            st.parts_lse[p:p + 1], B=sp.B, S=sp.S, H=sp.H, scale=sp.scale,
-                           num_splits=hint,
                            **({"block_table": st.block_table, "block_size": sp.block_size,
                                "num_blocks": w.kv.shape[0]} if sp.block_size else
                               {"kv_seq_stride": w.kv.shape[1]}))
+        # equal ranges: the automatic plan's chunk count, passed explicitly
+        a.num_splits = L.mla_decode_partial_plan(a, w.range_start[p:p + 1],
+                                                 w.range_end[p:p + 1]).equal_splits
         ws_ = torch.empty(max(1, L.mla_decode_partial_workspace_size(a)), dtype=torch.uint8,
                           device="cuda:0")
         a.workspace, a.workspace_bytes = ws_.data_ptr(), ws_.numel()

@@ -149,6 +149,56 @@ typedef struct mla_partial_args {
   unsigned flags;
 } mla_partial_args;
 
+/* How mla_decode_partial divides its work (the split rule it evaluates on
+ * the device from the range arrays), reported by mla_decode_partial_plan. */
+typedef struct mla_split_info {
+  int matrix_path;     /* 1: the matrix-core kernel (bf16 / fp16); 0: the plain
+                          kernel (fp32, or MLA_FLAG_FORCE_SIMPLE), which runs one
+                          workgroup per (range, query, head) and cuts nothing */
+  int chunk_tiles;     /* tiles of 32 keys per chunk of the automatic plan
+                          (num_splits == 0); 0 with an explicit num_splits */
+  int chunks;          /* chunks: each runs as one workgroup per query token
+                          and group of 128 heads */
+  int split_ranges;    /* ranges cut into more than one chunk (merged by LSE
+                          inside the call) */
+  int split_chunks;    /* chunks of those ranges (workspace slots in use) */
+  int equal_splits;    /* when every range is valid and has the same nonzero
+                          tile count: the chunk count per range the automatic
+                          plan gives (1 = no range is cut); passing it as
+                          num_splits yields the same pieces without the
+                          in-kernel plan. 0 otherwise. */
+  int max_chunks;      /* the launch's bound on `chunks` (grid size) */
+  int max_split_slots; /* the workspace's bound on `split_chunks` */
+} mla_split_info;
+
+/* The split plan of mla_decode_partial for `a` with the given ranges
+ * (K3 page, section 3.3: the chunk size chosen from the work and the
+ * compute units available). range_start / range_end are HOST copies of
+ * a->range_start / a->range_end ([P][B] int32); the argument struct is
+ * validated as by mla_decode_partial (its device pointers are not read).
+ * The rule, evaluated identically here and in the kernel: chunks of
+ * c0 = max(4, ceil(T S / 256)) tiles (T = all tiles of the valid ranges);
+ * when those make between one and two rounds of 256 workgroups, the smaller
+ * c1 = max(4, ceil(2 S T / (1024 - S U)), ceil(S T / 512)) (U = P B ranges)
+ * if its chunks fit in two rounds; a range of nt tiles becomes
+ * max(1, ceil(nt / c)) near-equal chunks, chunk i covering tiles
+ * [i nt / n, (i + 1) nt / n). With num_splits = k > 0 every range is cut
+ * into exactly k such pieces. Returns MLA_OK and fills `info`, or an error
+ * code (nothing is launched either way). */
+int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_start,
+                            const int32_t* range_end, mla_split_info* info);
+
+/* The pieces mla_decode_partial cuts a range into with num_splits = k:
+ * piece i of range [s, e) covers its tiles [i nt / k, (i + 1) nt / k) (nt =
+ * tiles of 32 logical positions the range touches, tile boundaries at
+ * multiples of 32), clipped to [s, e); a piece with no tile is empty
+ * (start = end). HOST arrays: range_start / range_end [n] in, piece_start /
+ * piece_end [k][n] out. Passing the pieces as k parts with num_splits = 1
+ * and merging them by LSE gives the call's own sub-range merge. Returns
+ * MLA_ERR_RANGE for a range with start < 0 or end < start. */
+int mla_cut_ranges(const int32_t* range_start, const int32_t* range_end, int n, int k,
+                   int32_t* piece_start, int32_t* piece_end);
+
 /* Bytes of device workspace mla_decode_partial needs for these arguments
  * (a pure function of the sizes, dtypes and flags; no device access).
  * Returns (size_t)-1 for invalid arguments. */
@@ -156,7 +206,19 @@ size_t mla_decode_partial_workspace_size(const mla_partial_args* a);
 
 /* Split-KV partial attention: for every part p, query token t and head h,
  * the softmax-weighted latent sum and LSE over p's visible keys (study page:
- * the HISTORY and CURRENT attention calls, each returning output + LSE). */
+ * the HISTORY and CURRENT attention calls, each returning output + LSE).
+ * bf16 / fp16 run on the matrix-core kernel for any H, in groups of 128
+ * heads that each read the part's keys once (a group with fewer real heads
+ * computes the missing rows from zero queries and never stores them); fp32
+ * (and MLA_FLAG_FORCE_SIMPLE) runs on the plain kernel, one workgroup per
+ * (part, query, head). S <= 64 (MLA_ERR_UNSUPPORTED above).
+ * Softmax range (K3 page, section 4.2: the online-softmax rescale is
+ * mandatory): the matrix kernel exponentiates relative to a per-chunk
+ * reference (bf16: 0, head maxima within +-64 in log2 units; fp16: each
+ * head's maximum over the chunk's first 32 keys, later keys at most 15
+ * log2 units above it, so fp16 weights stay below 2^15) and computes a
+ * chunk again with each head's exact maximum when its scores leave that
+ * window. Any finite scores give finite results. */
 int mla_decode_partial(const mla_partial_args* a, void* stream);
 
 /* q absorption: q_lat[t][h][c] = sum_j W_UK[h][c][j] * q_nope[t][h][j].

@@ -54,6 +54,15 @@ class PartialArgs(ctypes.Structure):
     ]
 
 
+class SplitInfo(ctypes.Structure):
+    _fields_ = [
+        ("matrix_path", ctypes.c_int), ("chunk_tiles", ctypes.c_int), ("chunks", ctypes.c_int),
+        ("split_ranges", ctypes.c_int), ("split_chunks", ctypes.c_int),
+        ("equal_splits", ctypes.c_int), ("max_chunks", ctypes.c_int),
+        ("max_split_slots", ctypes.c_int),
+    ]
+
+
 class PrologueArgs(ctypes.Structure):
     _fields_ = [
         ("q_nope", ctypes.c_void_p), ("q_pe", ctypes.c_void_p), ("w_uk", ctypes.c_void_p),
@@ -97,6 +106,12 @@ def lib():
                                       vp]
         L.mla_decode_prologue.restype = ci
         L.mla_decode_prologue.argtypes = [ctypes.POINTER(PrologueArgs), vp]
+        i32p = ctypes.POINTER(ctypes.c_int32)
+        L.mla_decode_partial_plan.restype = ci
+        L.mla_decode_partial_plan.argtypes = [ctypes.POINTER(PartialArgs), i32p, i32p,
+                                              ctypes.POINTER(SplitInfo)]
+        L.mla_cut_ranges.restype = ci
+        L.mla_cut_ranges.argtypes = [i32p, i32p, ci, ci, i32p, i32p]
         _lib = L
     return _lib
 
@@ -163,6 +178,39 @@ def mla_decode_partial_workspace_size(a: PartialArgs) -> int:
 
 def mla_decode_partial(a: PartialArgs, stream=None):
     _check(lib().mla_decode_partial(ctypes.byref(a), _stream(stream)), "mla_decode_partial")
+
+
+def _host_i32(a):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(a), dtype=np.int32)
+
+
+def _i32p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def mla_decode_partial_plan(a: PartialArgs, range_start, range_end) -> SplitInfo:
+    """The split plan mla_decode_partial evaluates for `a`, from host copies
+    of its [P][B] ranges (numpy or CPU arrays)."""
+    rs, re_ = _host_i32(range_start), _host_i32(range_end)
+    if rs.size != a.P * a.B or re_.size != a.P * a.B:
+        raise ValueError("ranges must hold P x B entries")
+    info = SplitInfo()
+    _check(lib().mla_decode_partial_plan(ctypes.byref(a), _i32p(rs), _i32p(re_),
+                                         ctypes.byref(info)), "mla_decode_partial_plan")
+    return info
+
+
+def mla_cut_ranges(range_start, range_end, k: int):
+    """Pieces [k][n] of the n ranges that num_splits = k cuts (host arrays)."""
+    import numpy as np
+    rs, re_ = _host_i32(range_start).ravel(), _host_i32(range_end).ravel()
+    n = rs.size
+    ps = np.empty((k, n), np.int32)
+    pe = np.empty((k, n), np.int32)
+    _check(lib().mla_cut_ranges(_i32p(rs), _i32p(re_), n, k, _i32p(ps), _i32p(pe)),
+           "mla_cut_ranges")
+    return ps, pe
 
 
 def mla_q_absorb(q_nope, w_uk, q_lat, stream=None):

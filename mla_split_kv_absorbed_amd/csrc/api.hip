@@ -164,6 +164,102 @@ int mla_decode_partial(const mla_partial_args* a, void* stream) {
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
+int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_start,
+                            const int32_t* range_end, mla_split_info* info) {
+  int st = check_partial_args(a);
+  if (st != MLA_OK) return st;
+  if (!range_start || !range_end || !info) return MLA_ERR_NULL;
+  const long long capacity = a->block_size > 0 ? (long long)a->max_blocks * a->block_size
+                                               : (long long)a->kv_seq_stride;
+  const long long U = (long long)a->P * a->B;
+  memset(info, 0, sizeof(*info));
+  info->matrix_path = use_mfma(a) ? 1 : 0;
+  if (!info->matrix_path) {
+    // the plain kernel: one workgroup per (range, query, head), no chunks
+    info->chunks = (int)U;
+    return MLA_OK;
+  }
+  const int hint = a->num_splits;
+  long long total = 0;
+  int nt0 = -1;
+  bool equal = true;
+  for (long long u = 0; u < U; ++u) {
+    const int s0 = range_start[u], e0 = range_end[u];
+    const int nt = range_bad(s0, e0, capacity) ? 0 : range_tiles(s0, e0);
+    if (range_bad(s0, e0, capacity) || nt == 0 || (nt0 >= 0 && nt != nt0)) equal = false;
+    nt0 = nt;
+    total += nt;
+  }
+  if (total > INT_MAX) return MLA_ERR_SHAPE;
+  // the automatic plan's chunk size (used when num_splits is 0)
+  int c_auto = chunk_tiles_one_round(total, a->S);
+  {
+    const int c1 = chunk_tiles_two_round(total, a->S, U);
+    if (c1 > 0 && c1 < c_auto) {
+      long long n0 = 0, n1 = 0;
+      for (long long u = 0; u < U; ++u) {
+        const int s0 = range_start[u], e0 = range_end[u];
+        const int nt = range_bad(s0, e0, capacity) ? 0 : range_tiles(s0, e0);
+        n0 += unit_chunks(nt, c_auto, 0);
+        n1 += unit_chunks(nt, c1, 0);
+      }
+      if (take_two_round(c_auto, c1, n0, n1, a->S)) c_auto = c1;
+    }
+  }
+  const int c = hint == 0 ? c_auto : 0;
+  long long chunks = 0, split_units = 0, split_chunks = 0;
+  for (long long u = 0; u < U; ++u) {
+    const int s0 = range_start[u], e0 = range_end[u];
+    const int nt = range_bad(s0, e0, capacity) ? 0 : range_tiles(s0, e0);
+    const int n = unit_chunks(nt, c, hint);
+    chunks += n;
+    if (n > 1) {
+      split_units += 1;
+      split_chunks += n;
+    }
+  }
+  // an explicit count cuts every range into exactly that many pieces (some
+  // may be empty) and splits every range when it exceeds 1
+  if (hint > 0) {
+    chunks = U * hint;
+    split_units = hint > 1 ? U : 0;
+    split_chunks = hint > 1 ? U * hint : 0;
+  }
+  info->chunk_tiles = c;
+  info->chunks = (int)chunks;
+  info->split_ranges = (int)split_units;
+  info->split_chunks = (int)split_chunks;
+  info->equal_splits = equal && U > 0 ? unit_chunks(nt0, c_auto, 0) : 0;
+  info->max_chunks = (int)plan_max_chunks(U, a->S, hint);
+  info->max_split_slots = (int)plan_max_split_slots(U, a->S, hint);
+  return MLA_OK;
+}
+
+int mla_cut_ranges(const int32_t* range_start, const int32_t* range_end, int n, int k,
+                   int32_t* piece_start, int32_t* piece_end) {
+  if (!range_start || !range_end || !piece_start || !piece_end) return MLA_ERR_NULL;
+  if (n < 1 || k < 1 || (long long)n * k > INT_MAX) return MLA_ERR_SHAPE;
+  for (int j = 0; j < n; ++j) {
+    const int a0 = range_start[j], e0 = range_end[j];
+    if (a0 < 0 || e0 < a0) return MLA_ERR_RANGE;
+  }
+  for (int j = 0; j < n; ++j) {
+    const int a0 = range_start[j], e0 = range_end[j];
+    const int nt = range_tiles(a0, e0), t0 = a0 / kTile;
+    for (int i = 0; i < k; ++i) {
+      int ps = a0, pe = a0;
+      if (nt > 0) {
+        const int lo = piece_tile(i, nt, k), hi = piece_tile(i + 1, nt, k);
+        ps = lo == 0 ? a0 : (t0 + lo) * kTile;
+        pe = hi > lo ? std::min(e0, (t0 + hi) * kTile) : ps;
+      }
+      piece_start[(size_t)i * n + j] = ps;
+      piece_end[(size_t)i * n + j] = pe;
+    }
+  }
+  return MLA_OK;
+}
+
 int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int part_dtype,
                     int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
                     void* out, int out_dtype, float* lse_out, void* stream) {

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include "mla_decode.h"
+#include "plan.h"
 
 namespace mla {
 
@@ -54,13 +55,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-
-// Plan of one partial-attention call: how every (part, sequence) key range is
-// cut into 32-token tiles and sub-ranges ("chunks"). Computed identically by
-// every workgroup that needs it (no planner launch, no descriptor buffer).
-constexpr int kTile = 32;          // keys per tile (one LDS stage)
-constexpr int kTargetGroups = 256; // workgroups one call aims to spread over
-constexpr int kMinChunkTiles = 4;  // never cut a range into pieces below this
 
 struct PartialParams {
   const void* q_lat;

@@ -11,8 +11,8 @@
 // Data flow per 32-token tile (one LDS stage of 32 x 576 x 2 B = 36 KB):
 //   HBM --buffer_load_dwordx4 ... lds--> LDS ring (4 stages, no VGPRs used)
 //   LDS --ds_read_b128--> key operand of S^T = K Q^T (32x32x16 MFMA, Q in VGPRs)
-//   softmax in registers (each lane holds 16 tokens of one head; fixed
-//   exponent reference, below) --> weights P to an LDS buffer
+//   softmax in registers (each lane holds 16 tokens of one head; exponent
+//   reference from the chunk's first tile, below) --> weights P to LDS
 //   LDS --ds_read_b64_tr_b16--> transposed value operand of O^T += C^T P^T
 // LDS layout of a stage is row-major, 1152 bytes per key row, with the 16-byte
 // chunks of row r permuted within each 128-byte group: chunk c sits at
@@ -27,15 +27,27 @@
 // instructions; the fp32 output O^T (128 x 128 per wave) stays in 256
 // accumulation registers (AGPRs).
 //
-// Softmax without rescaling the accumulators. The first pass uses the fixed
-// exponent reference 0: weights are 2^(score in log2 units). Floating-point
-// results are invariant under a common scale (the output is divided by the
-// same sum, the LSE adds the reference back), so this is exact as long as
-// every head's maximum lies in [-64, 64] (no overflow, no underflow of the
-// dominant weights). A chunk where some head leaves that window (adversarial
-// scores) is replayed once with each head's exact maximum as the reference.
-// The hot loop therefore never touches the output accumulators outside the
-// matrix instructions and needs no cross-lane maximum per tile.
+// Softmax without rescaling the accumulators. Weights are 2^(score - ref)
+// in log2 units with a fixed exponent reference per head and chunk.
+// Floating-point results are invariant under a common scale (the output is
+// divided by the same sum, the LSE adds the reference back), so this equals
+// the rescaled online softmax as long as the weights neither overflow nor
+// lose the dominant term, which depends on the weight type:
+//  - bf16 weights share fp32's exponent range: the reference is 0 and every
+//    head's maximum may lie anywhere in [-64, 64] (weights <= 2^64, the
+//    largest >= 2^-64);
+//  - fp16 weights overflow above 65504 and lose precision below 2^-14: the
+//    reference is each head's maximum over the chunk's first tile (kept in
+//    LDS, so the loop holds no extra register), and later scores may exceed
+//    it by at most 15 (weights <= 2^15; the dominant weight is >= 1).
+// A chunk where some head's maximum leaves its window is replayed once with
+// each head's exact maximum as the reference (weights <= 1). The hot loop
+// therefore never touches the output accumulators outside the matrix
+// instructions and needs no cross-lane maximum per tile.
+//
+// Heads come in groups of 128 (blockIdx.y): a group with fewer than 128
+// real heads (H not a multiple of 128) runs with zero queries in the missing
+// rows, whose results are never stored. The keys are read once per group.
 //
 // Step j of the tile loop: wait for tile j's loads and barrier; the score
 // product of tile j (one accumulation chain, key operands read 8 instructions
@@ -83,8 +95,6 @@ constexpr int kLoadsWave = kStageBytes / 16 / 64 / kWaves;  // 9
 constexpr int kKSteps = kRow / 16;             // 36
 constexpr int kDTiles = kDc / 32;              // 16
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kHeadroom = 64.0f;  // log2 units: first-pass weights stay <= 2^64
-constexpr float kFloor = 64.0f;     // ... and the largest one >= 2^-64
 constexpr int kIdCache = 256;                  // block ids staged in LDS per refill
 
 // chunk permutation inside a row: position = chunk ^ swz(row). The LDS has
@@ -131,6 +141,9 @@ __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt(MLA_V
 template <typename T> struct MT;
 template <> struct MT<bf16> {
   typedef bf16x8 v8;
+  // first pass: reference 0, head maxima within [-kWindow, kWindow]
+  static constexpr bool kTileRef = false;
+  static constexpr float kWindow = 64.0f;
   static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
@@ -147,6 +160,9 @@ template <> struct MT<bf16> {
 };
 template <> struct MT<f16> {
   typedef f16x8 v8;
+  // first pass: the first tile's maxima, later maxima at most kWindow above
+  static constexpr bool kTileRef = true;
+  static constexpr float kWindow = 15.0f;  // 2^15 < 65504
   static __device__ __forceinline__ floatx16 mfma(v8 a, v8 b, floatx16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
@@ -172,10 +188,6 @@ __device__ __forceinline__ void qk_drain(floatx16& a) {
 // the plan: tiles, chunks and split slots of one call, computed in-kernel
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int range_tiles(int st, int en) {
-  return en > st ? (en - 1) / kTile - st / kTile + 1 : 0;
-}
-
 struct Unit {
   int st, en;
   bool bad;
@@ -186,14 +198,9 @@ __device__ __forceinline__ Unit load_unit(const PartialParams& pp, int u) {
   Unit x;
   x.st = pp.range_start[u];
   x.en = pp.range_end[u];
-  x.bad = x.st < 0 || x.en < x.st || (long long)x.en > pp.capacity;
+  x.bad = range_bad(x.st, x.en, pp.capacity);
   x.nt = x.bad ? 0 : range_tiles(x.st, x.en);
   return x;
-}
-
-__device__ __forceinline__ int unit_chunks(int nt, int c, int hint) {
-  if (hint > 0) return min(hint, max(1, nt));
-  return max(1, (nt + c - 1) / c);
 }
 
 // Block-wide exclusive scans over the 256 threads: prefix sums within each
@@ -291,35 +298,19 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
   block_excl_scan<1>(tv, sh, tb_, tt);
   const int total = tt[0];
   Plan pl;
-  const long long want_groups = kTargetGroups;
-  const long long cw = ((long long)total * pp.S + want_groups - 1) / want_groups;
-  int c = (int)max((long long)kMinChunkTiles, cw);
-  // Chunks of c tiles give at most U + G / S chunks (G = kTargetGroups
-  // workgroups, S per chunk). Between one and two rounds of G workgroups,
-  // the second round is short and leaves most compute units idle at the
-  // end; a smaller chunk c1 that makes about two full rounds (U S / 2 for
-  // the rounding of each range, hence 2 S T / (4 G - U S)) is taken when
-  // its chunks still fit in two rounds. c1 >= S T / (2 G) keeps the chunk
-  // count within the grid bound max(U + G / S, 2 G / S) + 1, and split slots
-  // within 2 G / S.
+  // the chunk size of the split rule (plan.h): c0, or the two-round c1
+  int c = chunk_tiles_one_round(total, pp.S);
   {
-    const long long su = (long long)pp.S * U;
-    if (4LL * kTargetGroups > su) {
-      long long c1 = (2LL * pp.S * total + 4LL * kTargetGroups - su - 1) / (4LL * kTargetGroups - su);
-      c1 = max(c1, ((long long)total * pp.S + 2LL * kTargetGroups - 1) / (2LL * kTargetGroups));
-      c1 = max(c1, (long long)kMinChunkTiles);
-      if (c1 < c) {
-        int nv[2] = {0, 0}, nb[2], ntot[2];
-        for (int i = 0; i < u1 - u0; ++i) {
-          const int nt = unit_at(i).nt;
-          nv[0] += unit_chunks(nt, c, 0);
-          nv[1] += unit_chunks(nt, (int)c1, 0);
-        }
-        block_excl_scan<2>(nv, sh, nb, ntot);
-        if ((long long)pp.S * ntot[0] > kTargetGroups &&
-            (long long)pp.S * ntot[1] <= 2LL * kTargetGroups)
-          c = (int)c1;
+    const int c1 = chunk_tiles_two_round(total, pp.S, U);
+    if (c1 > 0 && c1 < c) {
+      int nv[2] = {0, 0}, nb[2], ntot[2];
+      for (int i = 0; i < u1 - u0; ++i) {
+        const int nt = unit_at(i).nt;
+        nv[0] += unit_chunks(nt, c, 0);
+        nv[1] += unit_chunks(nt, c1, 0);
       }
+      block_excl_scan<2>(nv, sh, nb, ntot);
+      if (take_two_round(c, c1, ntot[0], ntot[1], pp.S)) c = c1;
     }
   }
   pl.chunk_tiles = c;
@@ -371,8 +362,8 @@ __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Fou
       if (want >= off && want < off + n) {
         const int k = want - off;
         found->u = u0 + i;
-        found->tb = (int)((long long)k * x.nt / n);
-        found->te = (int)((long long)(k + 1) * x.nt / n);
+        found->tb = piece_tile(k, x.nt, n);
+        found->te = piece_tile(k + 1, x.nt, n);
         found->slot = n > 1 ? soff + k : -1;
         found->nsplit = n;
         found->split_idx = n > 1 ? poff : -1;
@@ -398,10 +389,7 @@ struct WsLayout {
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __host__ __device__ inline size_t slots_bound(int B, int S, int P, int hint) {
-  const size_t U = (size_t)P * B;
-  if (hint == 1) return 0;
-  if (hint > 1) return U * hint;
-  return (2 * kTargetGroups + S - 1) / S + 1;
+  return (size_t)plan_max_split_slots((long long)P * B, S, hint);
 }
 
 __host__ __device__ inline WsLayout ws_layout(int B, int S, int H, int P, int hint, int out_dtype) {
@@ -438,7 +426,8 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned m
                : "memory");
 }
 
-template <typename T>
+// kOneGroup: H == 128, one group of real heads (no head bound checks)
+template <typename T, bool kOneGroup>
 __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
   typedef typename MT<T>::v8 v8;
@@ -452,6 +441,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   // fp16, 16-byte chunks permuted by pchunk
   __shared__ __attribute__((aligned(16))) char sh_p[kHeadsGroup * kPRow];
   __shared__ float sh_inv[kHeadsGroup];
+  __shared__ float sh_mref[kHeadsGroup];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -500,8 +490,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     }
     const Unit x = load_unit(pp, u);
     fd.u = u;
-    fd.tb = (int)((long long)i * x.nt / k);
-    fd.te = (int)((long long)(i + 1) * x.nt / k);
+    fd.tb = piece_tile(i, x.nt, k);
+    fd.te = piece_tile(i + 1, x.nt, k);
     fd.slot = k > 1 ? u * k + i : -1;
     fd.nsplit = k;
     fd.split_idx = k > 1 ? u : -1;
@@ -510,13 +500,13 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     // a range shorter than k tiles has several pieces that start at tile 0:
     // piece 0 alone is the first
     first = i == 0;
-    if (blockIdx.x == 0 && tid == 0) *mp.ws_count = k > 1 ? pp.P * pp.B : 0;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *mp.ws_count = k > 1 ? pp.P * pp.B : 0;
     __syncthreads();
   } else {
     __syncthreads();
     const Plan pl = make_plan(pp, chunk, &sh_found, sh_scan);
     __syncthreads();
-    if (blockIdx.x == 0 && tid == 0) *mp.ws_count = pl.nsplit_units;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *mp.ws_count = pl.nsplit_units;
     fd.u = __builtin_amdgcn_readfirstlane(sh_found.u);
     if (fd.u < 0) return;  // grid slack beyond the plan's chunks
     fd.tb = __builtin_amdgcn_readfirstlane(sh_found.tb);
@@ -535,17 +525,19 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const int Tq = pp.B * S;
   const int st = fd.st;
   const int en = fd.en;
-  const bool unit_bad = st < 0 || en < st || (long long)en > pp.capacity;
+  const bool unit_bad = range_bad(st, en, pp.capacity);
   int vend = en;
   if (pp.mask == MLA_MASK_CAUSAL_WINDOW) vend = min(en, en - S + s + 1);
   // the first piece of a split range records where its pieces' results live
-  if (fd.split_idx >= 0 && first && s == 0 && tid == 0)
+  if (fd.split_idx >= 0 && first && s == 0 && blockIdx.y == 0 && tid == 0)
     mp.ws_desc[fd.split_idx] = intx4{fd.u, fd.slot, fd.nsplit, 0};
 
   // ---- per-lane constants -------------------------------------------------
   const int hi = lane >> 5;          // 0/1: which half of a 16-wide k step
   const int r32 = lane & 31;         // key row (QK) / head column
-  const int head = wave * kHeadsWave + r32;
+  const int head = wave * kHeadsWave + r32;  // head within the group
+  const int head0 = kOneGroup ? 0 : blockIdx.y * kHeadsGroup;  // the group's first head
+  const bool head_ok = kOneGroup || head0 + head < pp.H;
   // key operand of k step k: row r32, chunk 2k + hi, at
   // qk_off[k & 3] + (k >> 2) * 128
   int qk_off[4];
@@ -589,13 +581,21 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   // ---- Q^T for this wave's 32 heads, in registers -------------------------
   v8 q[kKSteps];
   {
-    const T* ql = (const T*)pp.q_lat + ((size_t)t * pp.H + head) * kDc;
-    const T* qr = (const T*)pp.q_rope + ((size_t)t * pp.H + head) * kDr;
+    // a missing head (beyond H) loads a real row and zeroes it: every lane
+    // issues the same loads
+    const int hq = head_ok ? head0 + head : pp.H - 1;
+    const T* ql = (const T*)pp.q_lat + ((size_t)t * pp.H + hq) * kDc;
+    const T* qr = (const T*)pp.q_rope + ((size_t)t * pp.H + hq) * kDr;
 #pragma unroll
     for (int k = 0; k < kKSteps; ++k) {
       const int d = k * 16 + hi * 8;
       q[k] = d < kDc ? *(const v8*)(ql + d) : *(const v8*)(qr + (d - kDc));
     }
+    if (!head_ok)
+#pragma unroll
+      for (int k = 0; k < kKSteps; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[k][i] = (T)0.f;
   }
   // The Q loads complete at the row table's wait (fill_rows), before the
   // first tile load: with nothing pending at loop entry the compiler places
@@ -608,9 +608,17 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   for (int i = 0; i < kDTiles; ++i)
 #pragma unroll
     for (int j = 0; j < 16; ++j) o[i][j] = 0.f;
-  // exponent reference (log2 units): 0 on the first pass, the head's exact
-  // maximum on a replay
+  // The head's exponent reference (log2 units): bf16 keeps it in m_ref (0
+  // on the first pass), fp16 in sh_mref (the maximum over the chunk's first
+  // tile); on a replay, the head's exact maximum. m_seen: the running
+  // maximum of the raw scores, for the replay decision.
   float m_ref = 0.f, m_seen = -INFINITY, l_part = 0.f, l_round = 0.f;
+  auto ref = [&]() __attribute__((always_inline)) -> float {
+    if constexpr (MT<T>::kTileRef)
+      return sh_mref[head];
+    else
+      return m_ref;
+  };
   bool bad = unit_bad;
   const float sl2 = pp.scale * kLog2e;
 
@@ -728,10 +736,12 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     // the unrounded ones. The running maximum of the raw scores is checked
     // after the pass.
     float pf_even = 0.f;
+    float mr = 0.f;
+    if constexpr (kSoft) mr = ref();
     auto weight = [&](int i) __attribute__((always_inline)) {
       const float sc = sa[i];
       m_seen = fmaxf(m_seen, sc);
-      const float pf = __builtin_amdgcn_exp2f(fmaf(sc, sl2, -m_ref));
+      const float pf = __builtin_amdgcn_exp2f(fmaf(sc, sl2, -mr));
       l_part += pf;
       if (i & 1) {
         pk[i >> 1] = t2{(T)pf_even, (T)pf};
@@ -798,7 +808,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) cv[i] = (T)0.f;
   };
-  auto step = [&](int j, int stage, bool has_prev) __attribute__((always_inline)) {
+  // take_ref: this is the chunk's first tile on the first pass (the
+  // exponent reference is taken from it)
+  auto step = [&](int j, int stage, bool has_prev, bool take_ref) __attribute__((always_inline)) {
     wait_vm(min(kAheadTiles - 1, seg_end - 1 - j));
     __syncthreads();
     // the loads of tile j + kAheadTiles go into the stage of tile j - 2,
@@ -863,7 +875,8 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     // The scores are read by vector instructions only after the result
     // latency of the last score product: behind qk_drain(), or, in the value
     // product, behind its first 4 matrix instructions (>= 128 cycles).
-    // mask (only a range's last tile can be partial; exp2(-inf) = 0)
+    // mask (a range's last tile, and the tiles the current-window mask
+    // reaches back over; exp2(-inf) = 0)
     const int tok0 = tile_tok0(j);
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
     if (nvis < kTile) {
@@ -883,12 +896,24 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     } else {
       // first tile of a segment: the weights alone (same arithmetic)
       qk_drain(sacc);
+      if (MT<T>::kTileRef && take_ref) {
+        // the chunk's first tile: the head's maximum over its 32 keys (16
+        // in each lane of the pair that holds the head) becomes the
+        // reference; a fully masked tile (the rest of the chunk is masked
+        // too) keeps 0
+        float mx = sacc[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sacc[i]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (hi == 0) sh_mref[head] = mx == -INFINITY ? 0.f : mx * sl2;
+      }
+      const float mr = ref();
       float pf_even = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float sc = sacc[i];
         m_seen = fmaxf(m_seen, sc);
-        const float pf = __builtin_amdgcn_exp2f(fmaf(sc, sl2, -m_ref));
+        const float pf = __builtin_amdgcn_exp2f(fmaf(sc, sl2, -mr));
         l_part += pf;
         if (i & 1) {
           pk[i >> 1] = t2{(T)pf_even, (T)pf};
@@ -915,7 +940,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
 
   // Tiles run in segments of up to kIdCache: the row table is refilled and
   // the load pipeline restarted between segments (outside the tile loop).
-  auto run_tiles = [&]() __attribute__((always_inline)) {
+  auto run_tiles = [&](bool first_pass) __attribute__((always_inline)) {
 #pragma clang loop unroll(disable)
     for (int seg = tb; seg < te; seg += kIdCache) {
       id_base = seg;
@@ -927,9 +952,9 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       next_id = tile_row(seg + kAheadTiles);
       pend_row = tile_row(seg + kAheadTiles + 1);
       zero_carry();
-      step(seg, 0, false);
+      step(seg, 0, false, first_pass && seg == tb);
 #pragma clang loop unroll(disable)
-      for (int j = seg + 1; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1), true);
+      for (int j = seg + 1; j < seg_end; ++j) step(j, (j - seg) & (kStages - 1), true, false);
       // the last tile's value product
       __syncthreads();
       const char* pl = lds + ((seg_end - 1 - seg) & (kStages - 1)) * kStageBytes;
@@ -946,23 +971,35 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     // land before the workgroup moves on or ends
     wait_vm_all();
   };
-  run_tiles();
+  run_tiles(true);
 
-  // replay the chunk with exact maxima if any head's maximum left the window
+  // replay the chunk with exact maxima if any head's maximum left its
+  // window (fp16: above the first-tile reference by more than kWindow; the
+  // maximum includes the first tile, so it never lies below it. bf16:
+  // outside [-kWindow, kWindow])
   const float m_head = fmaxf(m_seen, __shfl_xor(m_seen, 32, 64)) * sl2;
-  const bool over = m_head > kHeadroom || (m_head < -kFloor && m_head != -INFINITY);
+  bool over;
+  if constexpr (MT<T>::kTileRef)
+    over = m_head > sh_mref[head] + MT<T>::kWindow;
+  else
+    over = m_head > MT<T>::kWindow || (m_head < -MT<T>::kWindow && m_head != -INFINITY);
   if (__builtin_amdgcn_ballot_w64(over) && lane == 0) atomicOr(&sh_redo, 1 << wave);
   __syncthreads();
   const int redo = __builtin_amdgcn_readfirstlane(sh_redo);
   if (redo) {
-    m_ref = m_head == -INFINITY ? 0.f : m_head;
+    const float exact = m_head == -INFINITY ? 0.f : m_head;
+    if constexpr (MT<T>::kTileRef) {
+      if (hi == 0) sh_mref[head] = exact;
+    } else {
+      m_ref = exact;
+    }
     l_part = l_round = 0.f;
 #pragma unroll
     for (int d = 0; d < kDTiles; ++d)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[d][i] = 0.f;
     __syncthreads();
-    run_tiles();
+    run_tiles(false);
   }
 
   // ---- epilogue -------------------------------------------------------------
@@ -974,15 +1011,17 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     lse = NAN;
   } else if (l_tot > 0.f) {
     inv = 1.f / l_rnd;
-    lse = (m_ref + log2f(l_tot)) * 0.6931471805599453f;
+    lse = (ref() + log2f(l_tot)) * 0.6931471805599453f;
   } else {
     inv = 0.f;
     lse = -INFINITY;
   }
   // the normaliser of each head comes from the wave that ran its softmax
   if (hi == 0) sh_inv[head] = inv;
-  const size_t row0 = fd.slot < 0 ? ((size_t)p * Tq + t) * pp.H : ((size_t)fd.slot * S + s) * pp.H;
-  if (hi == 0) {
+  // first row of this group's heads in the part output (or the workspace)
+  const size_t row0 =
+      (fd.slot < 0 ? ((size_t)p * Tq + t) * pp.H : ((size_t)fd.slot * S + s) * pp.H) + head0;
+  if (hi == 0 && head_ok) {
     if (fd.slot < 0)
       store_any(pp.lse, row0 + head, pp.lse_dtype, lse);
     else
@@ -1021,10 +1060,13 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       }
       __syncthreads();
       char* out = (char*)(dst + (size_t)half * 64 * kDc);
+      // rows of missing heads (beyond H) are not stored
+      const int nrows = kOneGroup ? 64 : min(64, pp.H - head0 - half * 64);
 #pragma unroll
       for (int i = 0; i < 64 * kRowPieces / 256; ++i) {
         const int idx = tid + i * 256, r = idx / kRowPieces, c = idx % kRowPieces;
-        *(uint4*)(out + (size_t)r * kDc * kSz + c * 16) = *(const uint4*)(lds + r * kPitch + c * 16);
+        if (r < nrows)
+          *(uint4*)(out + (size_t)r * kDc * kSz + c * 16) = *(const uint4*)(lds + r * kPitch + c * 16);
       }
       __syncthreads();
     }
@@ -1135,16 +1177,12 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
 // ---------------------------------------------------------------------------
 
 bool mfma_path_supported(int dtype, int H, int block_size) {
-  return (dtype == MLA_BF16 || dtype == MLA_F16) && H == kHeadsGroup &&
+  return (dtype == MLA_BF16 || dtype == MLA_F16) && H >= 1 &&
          (block_size == 0 || block_size % kTile == 0);
 }
 
 size_t mfma_max_chunks(int B, int S, int P, int hint) {
-  const size_t U = (size_t)P * B;
-  if (hint > 0) return U * hint;
-  // the plan's chunk size gives at most U + G / S chunks, or 2 G / S when it
-  // takes the smaller size that fills two rounds
-  return std::max(U + (kTargetGroups + S - 1) / S, (size_t)(2 * kTargetGroups + S - 1) / S) + 1;
+  return (size_t)plan_max_chunks((long long)P * B, S, hint);
 }
 
 size_t mfma_workspace_bytes(int B, int S, int H, int P, int hint, int out_dtype) {
@@ -1163,11 +1201,20 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
   const size_t chunks = mfma_max_chunks(pp_in.B, pp_in.S, pp_in.P, pp_in.num_splits);
   size_t groups = chunks * pp_in.S;
   if (pp_in.S > 1) groups = (groups + 8 * pp_in.S - 1) / (8 * pp_in.S) * (8 * pp_in.S);
-  dim3 grid((unsigned)groups);
-  if (dtype == MLA_BF16)
-    hipLaunchKernelGGL(partial_mfma_kernel<bf16>, grid, dim3(256), 0, st, mp);
-  else
-    hipLaunchKernelGGL(partial_mfma_kernel<f16>, grid, dim3(256), 0, st, mp);
+  // blockIdx.y: the group of 128 heads
+  dim3 grid((unsigned)groups, (unsigned)((pp_in.H + kHeadsGroup - 1) / kHeadsGroup));
+  const bool one = pp_in.H == kHeadsGroup;
+  if (dtype == MLA_BF16) {
+    if (one)
+      hipLaunchKernelGGL((partial_mfma_kernel<bf16, true>), grid, dim3(256), 0, st, mp);
+    else
+      hipLaunchKernelGGL((partial_mfma_kernel<bf16, false>), grid, dim3(256), 0, st, mp);
+  } else {
+    if (one)
+      hipLaunchKernelGGL((partial_mfma_kernel<f16, true>), grid, dim3(256), 0, st, mp);
+    else
+      hipLaunchKernelGGL((partial_mfma_kernel<f16, false>), grid, dim3(256), 0, st, mp);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // no sub-splits requested: every range is written directly, nothing to merge

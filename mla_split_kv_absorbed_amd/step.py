@@ -16,13 +16,6 @@ import torch
 from . import _lib as L
 from .workloads import D_C, D_V, Workload
 
-# workgroups one partial-attention call aims to spread over (the kernel
-# planner's target; one per compute unit), keys per tile and the smallest
-# chunk the planner cuts (the library's own constants)
-TARGET_GROUPS = 256
-TILE = 32
-MIN_CHUNK_TILES = 4
-
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
@@ -33,71 +26,17 @@ def to_device(a: np.ndarray, dtype: str, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def split_hint(range_start: np.ndarray, range_end: np.ndarray, S: int) -> int:
-    """Sub-split count for mla_decode_partial from the host-side ranges.
-
-    When every range has the same length and the same number of 32-key tiles,
-    the kernel's automatic plan would cut each range into the same number of
-    chunks, longest first, which for equal ranges is range order. Passing
-    that count explicitly lets the kernel skip the plan. It is 1 (no
-    sub-splits) when the (range, query) units already fill the target
-    workgroup count. Otherwise the count mirrors the plan: chunks of
-    c = max(4, ceil(all tiles x S / 256)) tiles, or, when those make between
-    one and two rounds of 256 workgroups, the smaller chunk that fills two
-    rounds if its chunks fit in them. Ragged or empty ranges give 0 (let the
-    kernel plan)."""
-    st = np.asarray(range_start, np.int64).ravel()
-    en = np.asarray(range_end, np.int64).ravel()
-    if not st.size:
-        return 0
-    lens = en - st
-    if lens.min() != lens.max() or lens.min() <= 0:
-        return 0
-    tiles = (en - 1) // TILE - st // TILE + 1
-    if tiles.min() != tiles.max():
-        return 0
-    nt, units = int(tiles[0]), st.size
-    if units * S >= TARGET_GROUPS:
-        return 1
-    G, total = TARGET_GROUPS, units * nt
-    c = max(MIN_CHUNK_TILES, -(-total * S // G))
-    if 4 * G > S * units:
-        c1 = max(MIN_CHUNK_TILES, -(-2 * S * total // (4 * G - S * units)), -(-total * S // (2 * G)))
-        if c1 < c and S * units * -(-nt // c) > G and S * units * -(-nt // c1) <= 2 * G:
-            c = c1
-    return max(1, -(-nt // c))
-
-
-def cut_ranges(range_start: np.ndarray, range_end: np.ndarray, k: int):
-    """Each range [start, end) cut into k pieces on 32-key tile boundaries:
-    piece i takes tiles [i nt / k, (i + 1) nt / k) of the range's nt tiles
-    (the kernel's own cut), clipped to the range. Returns [k][n] starts and
-    ends; a piece with no tile is empty."""
-    st = np.asarray(range_start, np.int64).ravel()
-    en = np.asarray(range_end, np.int64).ravel()
-    out_st = np.zeros((k, st.size), np.int32)
-    out_en = np.zeros((k, st.size), np.int32)
-    for j, (a, e) in enumerate(zip(st, en)):
-        if e <= a:
-            out_st[:, j] = out_en[:, j] = a
-            continue
-        t0, nt = a // TILE, (e - 1) // TILE - a // TILE + 1
-        for i in range(k):
-            lo, hi = i * nt // k, (i + 1) * nt // k
-            ps = a if lo == 0 else (t0 + lo) * TILE
-            pe = min(e, (t0 + hi) * TILE) if hi > lo else ps
-            out_st[i, j], out_en[i, j] = ps, max(ps, pe)
-    return out_st, out_en
-
-
 class DecodeStep:
     """Device-resident inputs, outputs and workspace of one decode step."""
 
     def __init__(self, w: Workload, device="cuda", part_lse_dtype: Optional[str] = None,
                  num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None,
                  side_stream: bool = False, fused_tail: bool = True, keep_latent: bool = False,
-                 host_subranges: bool = False):
-        """host_subranges: a single part without a current chunk, whose
+                 host_subranges: bool = False, auto_plan: bool = False):
+        """num_splits: 0 lets the library plan; for equal ranges the plan's
+        chunk count is then passed explicitly (the kernel skips its plan)
+        unless auto_plan is set.
+        host_subranges: a single part without a current chunk, whose
         ranges the partial call would cut into k > 1 sub-ranges (equal ranges,
         bf16 / fp16), is instead cut on the host (cut_ranges) and passed as k
         parts, merged by the fused combine + V-up; the partial then runs
@@ -125,9 +64,9 @@ class DecodeStep:
         self.host_cut = 1
         if (host_subranges and P == 1 and not sp.current and num_splits == 0
                 and dt in ("bf16", "f16")):
-            k = split_hint(rs, re_, S)
+            k = self._plan(w, rs, re_, flags).equal_splits
             if k > 1:
-                rs, re_ = cut_ranges(rs, re_, k)
+                rs, re_ = L.mla_cut_ranges(rs, re_, k)
                 self.host_cut, P, self.P, num_splits = k, k, k, 1
         self.range_start = torch.from_numpy(np.ascontiguousarray(rs)).to(dev)
         self.range_end = torch.from_numpy(np.ascontiguousarray(re_)).to(dev)
@@ -142,9 +81,6 @@ class DecodeStep:
         self.out = torch.empty((T, H, D_V), dtype=self.dt, device=dev)
 
         explicit_splits = num_splits
-        if num_splits == 0:
-            num_splits = split_hint(w.range_start, w.range_end, S)
-        self.num_splits = num_splits
         kw = dict(B=B, S=S, H=H, scale=sp.scale, num_splits=num_splits, flags=flags)
         if sp.block_size > 0:
             kw.update(block_table=self.block_table, block_size=sp.block_size,
@@ -153,6 +89,12 @@ class DecodeStep:
             kw.update(kv_seq_stride=w.kv.shape[1])
         self.hist_args = L.partial_args(self.q_lat, self.q_rope, self.kv, self.range_start,
                                         self.range_end, self.parts_out, self.parts_lse, **kw)
+        # equal ranges: pass the automatic plan's chunk count explicitly, so
+        # the kernel cuts the same pieces without evaluating its plan
+        if num_splits == 0 and not auto_plan:
+            num_splits = L.mla_decode_partial_plan(self.hist_args, rs, re_).equal_splits
+            self.hist_args.num_splits = num_splits
+        self.num_splits = num_splits
         ws = L.mla_decode_partial_workspace_size(self.hist_args)
         self.cur = None
         if sp.current:
@@ -165,9 +107,10 @@ class DecodeStep:
                                            self.cur_end, self.cur_out, self.cur_lse,
                                            B=B, S=S, H=H, scale=sp.scale, kv_seq_stride=S,
                                            mask=L.MLA_MASK_CAUSAL_WINDOW,
-                                           num_splits=explicit_splits or split_hint(
-                                               np.zeros(B), np.full(B, S), S),
-                                           flags=flags)
+                                           num_splits=explicit_splits, flags=flags)
+            if explicit_splits == 0 and not auto_plan:
+                self.cur_args.num_splits = L.mla_decode_partial_plan(
+                    self.cur_args, np.zeros(B), np.full(B, S)).equal_splits
             ws = max(ws, L.mla_decode_partial_workspace_size(self.cur_args))
         self.workspace = torch.empty((max(ws, 1),), dtype=torch.uint8, device=dev)
         for a in [self.hist_args] + ([self.cur_args] if sp.current else []):
@@ -196,8 +139,29 @@ class DecodeStep:
                            and dt in ("bf16", "f16"))
         self.keep_latent = keep_latent or not self.fused_tail
 
-    def run(self, stream=None):
+    def _plan(self, w: Workload, rs, re_, flags) -> "L.SplitInfo":
+        """The library's split plan for a single part with these ranges (the
+        device pointers of the throwaway argument struct are never read)."""
+        sp = w.spec
+        dummy = torch.empty(1, dtype=self.dt)
+        lse = torch.empty(1, dtype=torch.float32)
+        kw = dict(B=sp.B, S=sp.S, H=sp.H, scale=sp.scale, flags=flags)
+        if sp.block_size > 0:
+            bt = torch.from_numpy(np.ascontiguousarray(w.block_table))
+            kw.update(block_table=bt, block_size=sp.block_size, num_blocks=w.kv.shape[0])
+        else:
+            kw.update(kv_seq_stride=w.kv.shape[1])
+        rs_t = torch.from_numpy(np.ascontiguousarray(rs, dtype=np.int32))
+        a = L.partial_args(dummy, dummy, dummy, rs_t, rs_t, dummy, lse, **kw)
+        return L.mla_decode_partial_plan(a, rs, re_)
+
+    def run(self, stream=None, marks: Optional[dict] = None):
+        """Enqueues one step. `marks` (optional) maps "current_done" and
+        "tail_start" to timing events, recorded after the current-chunk
+        partial (on its stream) and before the combine (on the main stream),
+        so a caller can check the order the streams ran in."""
         main = stream if stream is not None else torch.cuda.current_stream(self.dev)
+        marks = marks or {}
         if self.absorb:
             L.mla_q_absorb(self.q_nope, self.w_uk, self.q_lat, main)
         if self.side is not None:
@@ -205,6 +169,8 @@ class DecodeStep:
             self.ev_q.record(main)
             self.side.wait_event(self.ev_q)
             L.mla_decode_partial(self.cur_args, self.side)
+            if "current_done" in marks:
+                marks["current_done"].record(self.side)
             self.ev_cur.record(self.side)
             L.mla_decode_partial(self.hist_args, main)
             main.wait_event(self.ev_cur)
@@ -212,6 +178,10 @@ class DecodeStep:
             L.mla_decode_partial(self.hist_args, main)
             if self.w.spec.current:
                 L.mla_decode_partial(self.cur_args, main)
+                if "current_done" in marks:
+                    marks["current_done"].record(main)
+        if "tail_start" in marks:
+            marks["tail_start"].record(main)
         stream = main
         if self.fused_tail:
             L.mla_combine_vup(self.parts_out, self.parts_lse, self.w_uv, self.out, self.lse,

@@ -131,7 +131,9 @@ def test_prologue_then_attention():
     """A decode step from pre-rotation inputs: the prologue appends the S new
     tokens behind each sequence's history and rotates the query; partial
     attention over [0, L_b + S) with the current-window mask then matches the
-    oracle's latent attention over the oracle's updated cache."""
+    oracle's latent attention over the oracle's updated cache, with the
+    oracle's own rotated and absorbed queries (no GPU value enters the
+    oracle side)."""
     dt, B, S, H, bs = "bf16", 3, 2, 128, 32
     r = np.random.Generator(np.random.PCG64(21))
     lengths = np.array([700, 1000, 45], np.int32)  # history tokens (last block not full)
@@ -170,8 +172,9 @@ def test_prologue_then_attention():
     torch.cuda.synchronize()
     # oracle: prologue, then latent attention over each sequence's rows
     ql, qr, new = mo.decode_prologue(q_nope, q_pe, w_uk, kv_new, pos, cache, bt, bs, 0, B, S, D_C)
-    # the attention reads the queries as the prologue stored them
-    ql, qr = f64(q_lat), f64(q_rope)
+    # the oracle's own queries and appended rows, rounded once to the storage
+    # type (the query buffers and the cache hold that type)
+    ql, qr, new = W.round_to(ql, dt), W.round_to(qr, dt), W.round_to(new, dt)
     go, gl = f64(out[0]), f64(lse[0])
     heads = list(range(0, H, 11))
     for b in range(B):

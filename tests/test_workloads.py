@@ -75,48 +75,14 @@ def test_full_size_shapes_without_drawing_cache():
     assert L.min() >= 512 and L.max() <= 8192 and len(L) == 128
 
 
-def test_split_hint_policy():
-    """Host-side sub-split count: for ranges of equal length it is the count
-    the kernel's automatic plan would choose (1 once the (range, query) units
-    fill the target workgroup count); ragged or empty ranges leave the plan
-    to the kernel (0)."""
-    import numpy as np
-    from mla_split_kv_absorbed_amd.step import TARGET_GROUPS, split_hint
-    st = np.zeros((8, 32), np.int32)
-    en = np.full((8, 32), 4096, np.int32)
-    assert split_hint(st, en, 1) == 1                      # 256 equal units
-    # 32 units of 128 tiles: chunks of max(4, 4096 / 256) = 16 tiles -> 8 per range
-    assert split_hint(st[:1], en[:1], 1) == 8
-    # 4 units of 2 tiles: chunks of at least 4 tiles -> no cut
-    assert split_hint(st[:1, :4], np.full((1, 4), 64, np.int32), 1) == 1
-    # 16 units of 100 tiles x 2 queries: chunks of 13 tiles -> 8 per range
-    assert split_hint(np.zeros(16, np.int32), np.full(16, 3200, np.int32), 2) == 8
-    en2 = en.copy()
-    en2[0, 0] = 100
-    assert split_hint(st, en2, 1) == 0                     # ragged
-    assert split_hint(st, np.zeros_like(st), 1) == 0       # empty ranges
-    # equal lengths but a start inside a tile: different tile counts
-    assert split_hint(np.array([0, 16]), np.array([64, 80]), 1) == 0
-    assert split_hint(st[:4], en[:4], 2) == 1              # 128 units x 2 queries
-    # 40 units of 50 tiles: chunks of 8 tiles make 280 workgroups (one round
-    # and a short one); chunks of max(4, ceil(2 x 2000 / (1024 - 40)), ceil(2000 / 512)) = 5
-    # make 400, two rounds -> 10 per range
-    assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 1) == 10
-    # x 4 queries: chunks of 32 tiles make 320 workgroups; chunks of
-    # max(ceil(16000 / 864), ceil(8000 / 512)) = 19 make 480 -> 3 per range
-    assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 4) == 3
-    # x 8 queries: c = 63 makes 320 workgroups, but c1 = 46 would make 640,
-    # more than two rounds: 63 is kept -> 1 per range
-    assert split_hint(np.zeros(40, np.int32), np.full(40, 1600, np.int32), 8) == 1
-    assert TARGET_GROUPS == 256
-
-
 def test_cut_ranges_tiles_each_range_exactly():
-    """Host sub-ranges: k pieces per range, in order, disjoint, covering the
-    range, with inner boundaries on 32-key tiles, piece i holding tiles
+    """The library's range cut (mla_cut_ranges, the pieces num_splits = k
+    makes): k pieces per range, in order, disjoint, covering the range, with
+    inner boundaries on 32-key tiles, piece i holding tiles
     [i nt / k, (i + 1) nt / k); empty ranges give empty pieces."""
     import numpy as np
-    from mla_split_kv_absorbed_amd.step import cut_ranges
+    from mla_split_kv_absorbed_amd import _lib as L
+    cut_ranges = L.mla_cut_ranges
     rng = np.random.default_rng(5)
     st = rng.integers(0, 300, 64)
     en = st + rng.integers(0, 900, 64)
@@ -147,3 +113,13 @@ def test_cut_ranges_tiles_each_range_exactly():
             assert covered[0][0] == a and covered[-1][1] == e
             for (s0, e0), (s1, e1) in zip(covered, covered[1:]):
                 assert e0 == s1
+
+
+def test_cut_ranges_rejects_invalid_ranges():
+    import numpy as np
+    import pytest
+    from mla_split_kv_absorbed_amd import _lib as L
+    with pytest.raises(L.MLAError):
+        L.mla_cut_ranges(np.array([5]), np.array([4]), 2)
+    with pytest.raises(L.MLAError):
+        L.mla_cut_ranges(np.array([-1]), np.array([4]), 2)
