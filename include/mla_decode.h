@@ -221,6 +221,25 @@ size_t mla_decode_partial_workspace_size(const mla_partial_args* a);
  * window. Any finite scores give finite results. */
 int mla_decode_partial(const mla_partial_args* a, void* stream);
 
+/* mla_decode_partial without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). It runs the same kernels with
+ * the library's own device scratch as the workspace: a fixed array of
+ * mla_noalloc_scratch_bytes() (96 MiB) that every GPU the library runs on
+ * holds until the process ends (enough for every call with H <= 128 and
+ * 16-bit outputs under the automatic plan). a->workspace and
+ * a->workspace_bytes are ignored. The call allocates nothing; on a
+ * device's first call it looks up that device's scratch address (the
+ * stream's device must be current). Returns MLA_ERR_WORKSPACE when the
+ * call needs more than the scratch holds, otherwise as mla_decode_partial.
+ * Every call on one GPU shares that GPU's scratch: calls that overlap on
+ * one GPU (other streams or host threads) race and must be ordered by the
+ * caller. */
+int mla_decode_partial_noalloc(const mla_partial_args* a, void* stream);
+
+/* Bytes of the device scratch mla_decode_partial_noalloc uses. */
+size_t mla_noalloc_scratch_bytes(void);
+
 /* q absorption: q_lat[t][h][c] = sum_j W_UK[h][c][j] * q_nope[t][h][j].
  *   q_nope [T][H][128], w_uk [H][512][128], q_lat [T][H][512], all `dtype`.
  * (Not written out on the pages; it is the regrouping that lets the latent

@@ -110,6 +110,10 @@ def lib():
         L.mla_decode_partial_plan.restype = ci
         L.mla_decode_partial_plan.argtypes = [ctypes.POINTER(PartialArgs), i32p, i32p,
                                               ctypes.POINTER(SplitInfo)]
+        L.mla_decode_partial_noalloc.restype = ci
+        L.mla_decode_partial_noalloc.argtypes = [ctypes.POINTER(PartialArgs), vp]
+        L.mla_noalloc_scratch_bytes.restype = ctypes.c_size_t
+        L.mla_noalloc_scratch_bytes.argtypes = []
         L.mla_cut_ranges.restype = ci
         L.mla_cut_ranges.argtypes = [i32p, i32p, ci, ci, i32p, i32p]
         _lib = L
@@ -211,6 +215,17 @@ def mla_cut_ranges(range_start, range_end, k: int):
     _check(lib().mla_cut_ranges(_i32p(rs), _i32p(re_), n, k, _i32p(ps), _i32p(pe)),
            "mla_cut_ranges")
     return ps, pe
+
+
+def mla_decode_partial_noalloc(a: PartialArgs, stream=None):
+    """mla_decode_partial with the library's device scratch as workspace
+    (a.workspace is ignored)."""
+    _check(lib().mla_decode_partial_noalloc(ctypes.byref(a), _stream(stream)),
+           "mla_decode_partial_noalloc")
+
+
+def mla_noalloc_scratch_bytes() -> int:
+    return lib().mla_noalloc_scratch_bytes()
 
 
 def mla_q_absorb(q_nope, w_uk, q_lat, stream=None):

@@ -120,11 +120,29 @@ size_t mla_decode_partial_workspace_size(const mla_partial_args* a) {
 }
 
 int mla_decode_partial(const mla_partial_args* a, void* stream) {
+  if (!a) return MLA_ERR_NULL;
+  return mla::partial_call(a, a->workspace, a->workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace mla {
+
+size_t partial_workspace_need(const mla_partial_args* a) {
+  if (check_partial_args(a) != MLA_OK) return (size_t)-1;
+  return partial_ws_bytes(a);
+}
+
+// validation and launch of one partial call with the given workspace
+int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   int st = check_partial_args(a);
   if (st != MLA_OK) return st;
   const size_t need = partial_ws_bytes(a);
-  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  st = check_partial_alias(a, need > 0 ? a->workspace_bytes : 0);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  mla_partial_args chk = *a;
+  chk.workspace = workspace;
+  st = check_partial_alias(&chk, need > 0 ? workspace_bytes : 0);
   if (st != MLA_OK) return st;
 
   PartialParams pp;
@@ -155,7 +173,7 @@ int mla_decode_partial(const mla_partial_args* a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   if (use_mfma(a)) {
-    pp.ws_out = a->workspace;  // workspace base; the launcher lays it out
+    pp.ws_out = workspace;  // workspace base; the launcher lays it out
     pp.max_chunks = (int)mfma_max_chunks(a->B, a->S, a->P, a->num_splits);
     e = launch_partial_mfma(pp, a->q_dtype, s);
   } else {
@@ -163,6 +181,10 @@ int mla_decode_partial(const mla_partial_args* a, void* stream) {
   }
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
+
+}  // namespace mla
+
+extern "C" {
 
 int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_start,
                             const int32_t* range_end, mla_split_info* info) {

@@ -32,6 +32,13 @@ struct CombineParams {
   int part_dtype, lse_dtype, out_dtype;
 };
 
+// mla_decode_partial with an explicit workspace (validation, then launch);
+// returns an MLA status code
+int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_bytes,
+                 void* stream);
+// workspace bytes a partial call needs, (size_t)-1 for invalid arguments
+size_t partial_workspace_need(const mla_partial_args* a);
+
 hipError_t launch_partial_simple(const PartialParams& pp, int dtype, hipStream_t st);
 // MFMA path: q/kv dtype bf16 or f16, H % 128 == 0, block_size % 32 == 0 (or contiguous).
 bool mfma_path_supported(int dtype, int H, int block_size);

@@ -204,3 +204,19 @@ def prologue_base(**over):
 def test_prologue_validation(over, code):
     a = prologue_base(**over)
     assert L.lib().mla_decode_prologue(ctypes.byref(a), None) == code
+
+
+def test_noalloc_rejects_before_any_device_call():
+    """The allocation-free entry point validates like mla_decode_partial and
+    refuses a call whose workspace exceeds its scratch, all on the host."""
+    lib = L.lib()
+    assert L.mla_noalloc_scratch_bytes() == 96 << 20
+    assert lib.mla_decode_partial_noalloc(None, None) == -1
+    a = base_args()
+    a.q_lat = None
+    assert lib.mla_decode_partial_noalloc(ctypes.byref(a), None) == -1
+    # 512 heads under the automatic plan: 513 slots x 512 rows x 1028 B > 96 MiB
+    a = base_args(H=512)
+    need = lib.mla_decode_partial_workspace_size(ctypes.byref(a))
+    assert need > 96 << 20
+    assert lib.mla_decode_partial_noalloc(ctypes.byref(a), None) == -5
