@@ -108,16 +108,91 @@ __device__ __forceinline__ float merge_row(const CombineParams& c, size_t row, s
   return lse;
 }
 
+// Merge of R rows by one wave with every load issued before the first use:
+// lane i < np loads part i's LSE of each row, every lane loads its 8 values
+// of every part of every row, then the rows are merged with exactly the
+// arithmetic of merge_row (same order of the sums), so one memory round
+// trip serves all R rows. Up to kFastParts parts (the local part included);
+// more parts take merge_row, one row at a time. valid[r] false: row r is
+// neither loaded nor merged.
+constexpr int kFastParts = 8;
+
+template <typename TP, int R>
+__device__ __forceinline__ void merge_rows(const CombineParams& c, const size_t* row,
+                                           const bool* valid, size_t rows, int lane,
+                                           float (*o)[8], float* lse) {
+  const int np = c.P + (c.local_out ? 1 : 0);
+  if (np > kFastParts) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (valid[r]) lse[r] = merge_row<TP>(c, row[r], rows, lane, o[r]);
+    return;
+  }
+  typedef typename Vec8<TP>::v v8p;
+  float li[R];
+  v8p raw[R][kFastParts];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    li[r] = -INFINITY;
+    if (valid[r] && lane < np) li[r] = part_lse(c, lane, row[r], rows);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int k = 0; k < kFastParts; ++k)
+      if (valid[r] && k < np) {
+        const TP* src = k < c.P ? (const TP*)c.parts_out + ((size_t)k * rows + row[r]) * kDc
+                                : (const TP*)c.local_out + row[r] * kDc;
+        raw[r][k] = *(const v8p*)(src + lane * 8);
+      }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (!valid[r]) continue;
+    const bool nan_seen = __builtin_amdgcn_ballot_w64(isnan(li[r])) != 0;
+    const float m = wave_max(li[r]);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float z = 0.f;
+    if (m != -INFINITY && !nan_seen) {
+      const float wl = li[r] == -INFINITY ? 0.f : expf(li[r] - m);
+#pragma unroll
+      for (int k = 0; k < kFastParts; ++k) {
+        if (k < np) {
+          const float w = __shfl(wl, k, 64);
+          z += w;
+          if (w != 0.f)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)raw[r][k][e], acc[e]);
+        }
+      }
+    }
+    if (nan_seen) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] = NAN;
+      lse[r] = NAN;
+    } else if (z > 0.f) {
+      const float inv = 1.f / z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] = acc[e] * inv;
+      lse[r] = m + logf(z);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[r][e] = 0.f;
+      lse[r] = -INFINITY;
+    }
+  }
+}
+
 template <typename TP, typename TO>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams c) {
   const int lane = threadIdx.x & 63;
   const size_t rows = (size_t)c.T * c.H;
   const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
-  float o[8];
-  const float lse = merge_row<TP>(c, row, rows, lane, o);
-  store8<TO>((TO*)c.out + row * kDc + lane * 8, o);
-  if (c.lse_out && lane == 0) c.lse_out[row] = lse;
+  float o[1][8], lse[1];
+  const bool valid[1] = {true};
+  merge_rows<TP, 1>(c, &row, valid, rows, lane, o, lse);
+  store8<TO>((TO*)c.out + row * kDc + lane * 8, o[0]);
+  if (c.lse_out && lane == 0) c.lse_out[row] = lse[0];
 }
 
 template <typename TP>
@@ -199,23 +274,39 @@ __global__ __launch_bounds__(kCvThreads) void combine_vup_kernel(CombineVupParam
       st[p][i] = *(const v8*)(wsrc + (size_t)cc * kDv + p * kCvCols + q * 8);
     }
 
-  // merged latent rows of the block, rounded to T as a stored latent would be
-  for (int r = wave; r < 32; r += kCvWaves) {
-    v8 xv;
-    if (r < nt) {
-      const size_t row = (size_t)(t0 + r) * c.H + h;
-      float o[8];
-      const float lse = merge_row<TP>(c, row, rows, lane, o);
+  // merged latent rows of the block (wave w: rows w and w + 16, both in
+  // flight together for 16-bit parts, one after the other for fp32 parts),
+  // rounded to T as a stored latent would be
+  constexpr int kRows = 32 / kCvWaves;                    // rows per wave
+  constexpr int kR = sizeof(TP) == 4 ? 1 : kRows;         // rows in flight
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = from_f<T>(o[e]);
-      if (cv.lat_out) *(v8*)((T*)cv.lat_out + row * kDc + lane * 8) = xv;
-      if (c.lse_out && lane == 0) c.lse_out[row] = lse;
-    } else {
-      // columns past the block: their products are never stored
+  for (int i0 = 0; i0 < kRows; i0 += kR) {
+    size_t row[kR];
+    bool valid[kR];
+    float o[kR][8], lse[kR];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = (T)0.f;
+    for (int i = 0; i < kR; ++i) {
+      const int r = wave + (i0 + i) * kCvWaves;
+      valid[i] = r < nt;
+      row[i] = (size_t)(t0 + (valid[i] ? r : 0)) * c.H + h;
     }
-    *(v8*)(xl + r * kCvXRow + lane * 16) = xv;
+    merge_rows<TP, kR>(c, row, valid, rows, lane, o, lse);
+#pragma unroll
+    for (int i = 0; i < kR; ++i) {
+      const int r = wave + (i0 + i) * kCvWaves;
+      v8 xv;
+      if (valid[i]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = from_f<T>(o[i][e]);
+        if (cv.lat_out) *(v8*)((T*)cv.lat_out + row[i] * kDc + lane * 8) = xv;
+        if (c.lse_out && lane == 0) c.lse_out[row[i]] = lse[i];
+      } else {
+        // columns past the block: their products are never stored
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xv[e] = (T)0.f;
+      }
+      *(v8*)(xl + r * kCvXRow + lane * 16) = xv;
+    }
   }
 
   const int r32 = lane & 31, hi = lane >> 5;

@@ -101,65 +101,97 @@ __device__ __forceinline__ void absorb_block(const T* __restrict__ qn, const T* 
   }
 }
 
-// q absorption over many token blocks: grid (H, 2 halves of c, ceil(blocks /
-// kAbsorbBlocks)); each wave keeps its two W_UK tiles in registers and walks
-// up to kAbsorbBlocks 32-token blocks, loading the next block's q_nope while
-// the current one is multiplied, so W_UK[h] is read once per kAbsorbBlocks
-// blocks instead of once per block.
-constexpr int kAbsorbBlocks = 4;
+// q absorption of the decode step: grid (H, 4 quarters of c, ceil(T / 128)
+// token groups), 4 waves. The workgroup's 128 rows of W_UK[h] (32 KB) and
+// its tokens' q_nope[t][h] rows (256 B each) are staged in LDS by direct
+// loads, every instruction covering whole 256-byte rows (four per
+// instruction), so each cache line is fetched once; the operands are then
+// read from LDS in the matrix layout. Wave w computes c rows 32 w .. of the
+// quarter for every 32-token block of the group, and the results go out
+// through LDS again, one 256-byte row per token. LDS rows are 16 chunks of
+// 16 B with chunk c of row r at position c ^ (r & 15), which keeps the
+// operand reads (16 rows per read) free of bank conflicts.
+constexpr int kAbsRows = 128;  // c rows per workgroup
+constexpr int kAbsTok = 128;   // tokens per workgroup
+constexpr int kAbsRowB = kDn * 2;  // 256 bytes per LDS row
+
+__device__ __forceinline__ int abs_pos(int chunk, int row) { return (chunk ^ (row & 15)) << 4; }
 
 template <typename T>
 __global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ qn,
                                                           const T* __restrict__ wuk,
                                                           T* __restrict__ ql, int Tn, int H) {
   typedef typename GT<T>::v8 v8;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = blockIdx.x;
-  const int c0 = blockIdx.y * 256 + wave * 64;
-  const int r = lane & 31, hi = lane >> 5;
-  const int nblk = (Tn + 31) / 32;
-  const int b0 = blockIdx.z * kAbsorbBlocks, b1 = min(nblk, b0 + kAbsorbBlocks);
-  // B = q_nope^T of block tb: column t, 8 consecutive j per k step (rows past
-  // Tn load the last valid row and are never stored)
-  auto load_b = [&](int tb, v8* b) __attribute__((always_inline)) {
-    const int tl = min(tb * 32 + r, Tn - 1);
+  __shared__ __attribute__((aligned(1024))) char wl[kAbsRows * kAbsRowB];  // W rows, then the results
+  __shared__ __attribute__((aligned(1024))) char qs[kAbsTok * kAbsRowB];   // q_nope rows
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = blockIdx.x, c0 = blockIdx.y * kAbsRows, t0 = blockIdx.z * kAbsTok;
+  const int nt = min(kAbsTok, Tn - t0);
+  // W_UK[h][c0 + r][:]: 128 contiguous rows. Load i of wave w fills rows
+  // 4 (8 w + i) .. + 3: lane l takes row 4 (8 w + i) + l / 16, LDS position
+  // l % 16, i.e. the row's chunk (l % 16) ^ (row % 16).
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(wuk + ((size_t)h * kDc + c0) * kDn), (short)0, kAbsRows * kAbsRowB, 0x00020000);
+  // q_nope[t0 + j][h][:]: rows H * 256 bytes apart; tokens past Tn fall
+  // outside the records and load zeros
+  const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(qn + ((size_t)t0 * H + h) * kDn), (short)0, ((nt - 1) * H + 1) * kAbsRowB,
+      0x00020000);
 #pragma unroll
-    for (int k = 0; k < kDn / 16; ++k)
-      b[k] = *(const v8*)(qn + ((size_t)tl * H + h) * kDn + k * 16 + hi * 8);
-  };
-  v8 a[2][kDn / 16];
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const T* wr = wuk + ((size_t)h * kDc + c0 + ct * 32 + r) * kDn + hi * 8;
-#pragma unroll
-    for (int k = 0; k < kDn / 16; ++k) a[ct][k] = *(const v8*)(wr + k * 16);
+  for (int i = 0; i < 8; ++i) {
+    const int row = 4 * (8 * wave + i) + (lane >> 4);
+    const int pos = abs_pos(lane & 15, row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (LDS_AS void*)(wl + (8 * wave + i) * 1024), 16,
+                                             row * kAbsRowB + pos, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (LDS_AS void*)(qs + (8 * wave + i) * 1024), 16,
+                                             row * H * kAbsRowB + pos, 0, 0, 0);
   }
-  v8 b[2][kDn / 16];
-  load_b(b0, b[0]);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's rows landed
+  __syncthreads();
+
+  const int r = lane & 31, hi = lane >> 5;
+  // A = W rows 32 wave + r, 8 consecutive j per k step
+  v8 a[kDn / 16];
 #pragma unroll
-  for (int i = 0; i < kAbsorbBlocks; ++i) {
-    const int tb = b0 + i;
-    if (tb >= b1) break;
-    if (tb + 1 < b1) load_b(tb + 1, b[(i + 1) & 1]);
-    const int t = tb * 32 + r;
+  for (int k = 0; k < kDn / 16; ++k)
+    a[k] = *(const v8*)(wl + (32 * wave + r) * kAbsRowB + abs_pos(2 * k + hi, r));
+  const int nblk = (nt + 31) / 32;
+  floatx16 acc[kAbsTok / 32];
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      floatx16 acc;
+  for (int bk = 0; bk < kAbsTok / 32; ++bk) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[bk][e] = 0.f;
+    if (bk < nblk) {
 #pragma unroll
-      for (int k = 0; k < kDn / 16; ++k) acc = GT<T>::mfma(a[ct][k], b[i & 1][k], acc);
-      if (t < Tn) {
-        T* dst = ql + ((size_t)t * H + h) * kDc + c0 + ct * 32 + 4 * hi;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          typename GT<T>::v4 v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = (T)acc[4 * g + e];
-          *(typename GT<T>::v4*)(dst + 8 * g) = v;
-        }
+      for (int k = 0; k < kDn / 16; ++k) {
+        const v8 b = *(const v8*)(qs + (32 * bk + r) * kAbsRowB + abs_pos(2 * k + hi, r));
+        acc[bk] = GT<T>::mfma(a[k], b, acc[bk]);
       }
     }
+  }
+  __syncthreads();  // every wave is done reading W: its rows take the results
+  // result of token 32 bk + r, c rows 32 wave + 8 g + 4 hi .. + 3: 8 bytes at
+  // chunk 4 wave + g, half hi of LDS row 32 bk + r
+#pragma unroll
+  for (int bk = 0; bk < kAbsTok / 32; ++bk) {
+    if (bk < nblk) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        typename GT<T>::v4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (T)acc[bk][4 * g + e];
+        *(typename GT<T>::v4*)(wl + (32 * bk + r) * kAbsRowB + abs_pos(4 * wave + g, r) + 8 * hi) = v;
+      }
+    }
+  }
+  __syncthreads();
+  // one 256-byte row per token: q_lat[t0 + row][h][c0 .. c0 + 127]
+#pragma unroll
+  for (int i = 0; i < kAbsTok * 16 / 256; ++i) {
+    const int idx = tid + i * 256, row = idx >> 4, ch = idx & 15;
+    if (row < nt)
+      *(uint4*)(ql + ((size_t)(t0 + row) * H + h) * kDc + c0 + ch * 8) =
+          *(const uint4*)(wl + row * kAbsRowB + abs_pos(ch, row));
   }
 }
 
@@ -253,7 +285,7 @@ static_assert(kVupChunks * kVupThreads * 16 == kDc * kVupCols * 2, "V-up staging
 
 hipError_t launch_absorb_mfma(const void* qn, const void* w, void* ql, int Tn, int H, int dt,
                               hipStream_t st) {
-  dim3 g(H, kDc / 256, ((Tn + 31) / 32 + kAbsorbBlocks - 1) / kAbsorbBlocks);
+  dim3 g(H, kDc / kAbsRows, (Tn + kAbsTok - 1) / kAbsTok);
   if (dt == MLA_BF16)
     hipLaunchKernelGGL(absorb_mfma_kernel<bf16>, g, dim3(256), 0, st, (const bf16*)qn,
                        (const bf16*)w, (bf16*)ql, Tn, H);
