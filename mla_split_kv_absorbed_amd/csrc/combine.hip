@@ -251,7 +251,8 @@ constexpr int kCvThreads = kCvWaves * 64;
 constexpr int kCvPieces = kDc * kCvCols * 2 / 16 / kCvThreads;  // 16-byte W pieces per thread per pass
 static_assert(kCvPieces * kCvThreads * 16 == kDc * kCvCols * 2, "W pass split");
 
-template <typename TP, typename T>
+// kTb: tokens per workgroup (16 or 32), cv.tb
+template <typename TP, typename T, int kTb>
 __global__ __launch_bounds__(kCvThreads) void combine_vup_kernel(CombineVupParams cv) {
   typedef typename CvT<T>::v8 v8;
   __shared__ __attribute__((aligned(16))) char wl[kDc * kCvWRow];
@@ -259,8 +260,8 @@ __global__ __launch_bounds__(kCvThreads) void combine_vup_kernel(CombineVupParam
   const CombineParams& c = cv.c;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = blockIdx.x;
-  const int t0 = blockIdx.y * cv.tb;
-  const int nt = min(cv.tb, c.T - t0);
+  const int t0 = blockIdx.y * kTb;
+  const int nt = min(kTb, c.T - t0);
   const size_t rows = (size_t)c.T * c.H;
 
   // W_UV[h][:, 64 p .. 64 p + 63] for both passes p: 512 rows x 128 B each
@@ -274,11 +275,19 @@ __global__ __launch_bounds__(kCvThreads) void combine_vup_kernel(CombineVupParam
       st[p][i] = *(const v8*)(wsrc + (size_t)cc * kDv + p * kCvCols + q * 8);
     }
 
-  // merged latent rows of the block (wave w: rows w and w + 16, both in
-  // flight together for 16-bit parts, one after the other for fp32 parts),
-  // rounded to T as a stored latent would be
-  constexpr int kRows = 32 / kCvWaves;                    // rows per wave
+  // merged latent rows of the block (wave w: rows w and, with 32 tokens,
+  // w + 16, both in flight together for 16-bit parts, one after the other
+  // for fp32 parts), rounded to T as a stored latent would be; the rows of
+  // a 16-token block past 16 are zero
+  constexpr int kRows = kTb / kCvWaves;                   // rows per wave
   constexpr int kR = sizeof(TP) == 4 ? 1 : kRows;         // rows in flight
+  if (kTb < 32) {
+    v8 z;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (T)0.f;
+#pragma unroll
+    for (int r = kTb + wave; r < 32; r += kCvWaves) *(v8*)(xl + r * kCvXRow + lane * 16) = z;
+  }
 #pragma unroll
   for (int i0 = 0; i0 < kRows; i0 += kR) {
     size_t row[kR];
@@ -353,12 +362,20 @@ __global__ __launch_bounds__(kCvThreads) void combine_vup_kernel(CombineVupParam
   }
 }
 
+template <typename TP, typename T>
+static void launch_combine_vup_tb(const CombineVupParams& cv, dim3 g, hipStream_t st) {
+  if (cv.tb == 16)
+    hipLaunchKernelGGL((combine_vup_kernel<TP, T, 16>), g, dim3(kCvThreads), 0, st, cv);
+  else
+    hipLaunchKernelGGL((combine_vup_kernel<TP, T, 32>), g, dim3(kCvThreads), 0, st, cv);
+}
+
 template <typename TP>
 static void launch_combine_vup_t(const CombineVupParams& cv, dim3 g, hipStream_t st) {
   if (cv.c.out_dtype == MLA_BF16)
-    hipLaunchKernelGGL((combine_vup_kernel<TP, bf16>), g, dim3(kCvThreads), 0, st, cv);
+    launch_combine_vup_tb<TP, bf16>(cv, g, st);
   else
-    hipLaunchKernelGGL((combine_vup_kernel<TP, f16>), g, dim3(kCvThreads), 0, st, cv);
+    launch_combine_vup_tb<TP, f16>(cv, g, st);
 }
 
 hipError_t launch_combine_vup(const CombineVupParams& cv, hipStream_t st) {

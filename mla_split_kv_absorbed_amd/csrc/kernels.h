@@ -50,7 +50,7 @@ size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits, int out_
 hipError_t launch_combine(const CombineParams& c, hipStream_t st);
 
 // combine fused with V-up: c.out_dtype is the compute type (bf16 / f16) of
-// w_uv, out and lat_out; tokens per workgroup tb in [1, 32]
+// w_uv, out and lat_out; tokens per workgroup tb: 16 or 32
 struct CombineVupParams {
   CombineParams c;
   const void* w_uv;
