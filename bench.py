@@ -115,8 +115,8 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
         "kernel": "partial_mfma_kernel<bf16>",
         "workload": "config2:bf16_B32_H128_L32768_paged32_8parts",
         "kernel_sha": kernel_hash(),
-        "kernel_sha_of": "bench.kernel_hash(): partial_mfma.hip, common.h and kernels.h with "
-                         "comments and blank lines dropped",
+        "kernel_sha_of": "bench.kernel_hash(): partial_mfma.hip, common.h, kernels.h and plan.h "
+                         "with comments and blank lines dropped",
         "fetch_kib_per_dispatch": round(fetch, 3),
         "write_kib_per_dispatch": round(write, 3),
         "dispatches": {"fetch": nf, "write": nw},
@@ -142,15 +142,21 @@ SQ_PASSES = (
 )
 
 
-def sq_summary(dirs):
+def sq_summary(dirs, last: int = 0):
     """Matrix-core and LDS counters of the partial kernel's decode-step launch
     (the all-parts history call: the longest partial_mfma_kernel dispatches),
-    from rocprofv3 --pmc runs of the SQ_PASSES counter sets, as markdown."""
+    from rocprofv3 --pmc runs of the SQ_PASSES counter sets, as markdown.
+    last > 0: only the last `last` such launches of each run (the steady
+    state after a settle phase)."""
     import csv
     vals, durs = {}, []
     for d in dirs:
         with open(os.path.join(d, "run_counter_collection.csv")) as f:
             rows = _step_launches(list(csv.DictReader(f)))
+        if last > 0:
+            ids = sorted({int(r["Dispatch_Id"]) for r in rows})[-last:]
+            keep = set(ids)
+            rows = [r for r in rows if int(r["Dispatch_Id"]) in keep]
         if not rows:
             raise SystemExit(f"no partial_mfma_kernel dispatch in {d}")
         grid = int(rows[0]["Grid_Size"])
@@ -279,12 +285,14 @@ def main():
                                                        "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
                     help="write the partial kernel's HBM traffic file from four rocprofv3 "
                          "--pmc output directories (no GPU needed)")
+    ap.add_argument("--sq-last", type=int, default=0,
+                    help="with --sq-summary: only the last N decode-step launches of each run")
     ap.add_argument("--sq-summary", nargs=2, metavar=("PASS1_DIR", "PASS2_DIR"),
                     help="print the partial kernel's matrix-core and LDS counters (two rocprofv3 "
                          "--pmc runs of the SQ_PASSES sets) as markdown (no GPU needed)")
     args = ap.parse_args()
     if args.sq_summary:
-        print(sq_summary(args.sq_summary), end="", flush=True)
+        print(sq_summary(args.sq_summary, args.sq_last), end="", flush=True)
         return
     if args.pmc_summary:
         dirs = args.pmc_summary
