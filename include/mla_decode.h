@@ -34,6 +34,10 @@
  *    returns MLA_ERR_HIP. Device faults surface at the caller's next sync.
  *  - Outputs must not overlap inputs (checked where the extents are known:
  *    MLA_ERR_ALIAS).
+ *  - The row tensors (queries, cache, partial outputs and parts, weights,
+ *    outputs, workspace) are accessed 16 bytes at a time: their pointers
+ *    must be 16-byte aligned (MLA_ERR_RANGE otherwise; checked after the
+ *    overlap check). LSE and int32 arrays need only their element alignment.
  *  - Results are bitwise reproducible for identical inputs and arguments
  *    (fixed reduction orders, no floating-point atomics).
  *  - Accumulation is fp32; results are rounded to nearest-even into the
@@ -272,7 +276,9 @@ int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int par
  *   w_uv [H][512][128] (dtype); out [T][H][128] (dtype) == [T][H*128];
  *   lse_out fp32 [T][H] or NULL; lat_out [T][H][512] (dtype) or NULL: the
  *   merged latent as mla_lse_combine writes it.
- * Outputs must not overlap the inputs or each other (MLA_ERR_ALIAS). */
+ * Outputs must not overlap the inputs or each other (MLA_ERR_ALIAS).
+ * MLA_ERR_SHAPE: T < 1, H outside [1, 65535], or T * H so large that the
+ * launch would need more than 2^30 workgroups. */
 int mla_combine_vup(const void* parts_out, const void* parts_lse, int P, int part_dtype,
                     int lse_dtype, const void* local_out, const void* local_lse, int T, int H,
                     const void* w_uv, int dtype, void* out, float* lse_out, void* lat_out,

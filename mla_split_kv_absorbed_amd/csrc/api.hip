@@ -5,6 +5,9 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+#include <initializer_list>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +37,15 @@ bool any_overlap(const Extent* outs, int no, const Extent* ins, int ni) {
     for (int j = i + 1; j < no; ++j)
       if (overlap(outs[i], outs[j])) return true;
   }
+  return false;
+}
+
+// The row tensors (queries, cache, parts, weights, outputs, workspace) are
+// read and written with 16-byte and LDS-direct accesses: their base pointers
+// must be 16-byte aligned (NULL entries are skipped).
+bool any_misaligned(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p && ((uintptr_t)p & 15)) return true;
   return false;
 }
 
@@ -90,7 +102,10 @@ int check_partial_alias(const mla_partial_args* a, size_t ws) {
   Extent outs[3] = {{a->out, P * T * H * kDc * elem_bytes(a->out_dtype)},
                     {a->lse, P * T * H * elem_bytes(a->lse_dtype)},
                     {a->workspace, ws}};
-  return any_overlap(outs, 3, ins, 6) ? MLA_ERR_ALIAS : MLA_OK;
+  if (any_overlap(outs, 3, ins, 6)) return MLA_ERR_ALIAS;
+  if (any_misaligned({a->q_lat, a->q_rope, a->kv, a->out, ws ? a->workspace : nullptr}))
+    return MLA_ERR_RANGE;
+  return MLA_OK;
 }
 
 }  // namespace
@@ -302,6 +317,7 @@ int mla_lse_combine(const void* parts_out, const void* parts_lse, int P, int par
   Extent outs[2] = {{out, rows * kDc * elem_bytes(out_dtype)},
                     {lse_out, lse_out ? rows * 4 : 0}};
   if (any_overlap(outs, 2, ins, 4)) return MLA_ERR_ALIAS;
+  if (any_misaligned({parts_out, local_out, out})) return MLA_ERR_RANGE;
   CombineParams c;
   c.parts_out = parts_out;
   c.parts_lse = parts_lse;
@@ -330,11 +346,15 @@ int mla_combine_vup(const void* parts_out, const void* parts_lse, int P, int par
   if (P < 0 || T < 1 || H < 1 || H > 65535) return MLA_ERR_SHAPE;
   if (P + (local_out ? 1 : 0) < 1) return MLA_ERR_SHAPE;
   if (dtype == MLA_F32) return MLA_ERR_UNSUPPORTED;
-  // tokens per workgroup: 16 when that makes at most 256 workgroups (about
-  // one per CU: small batches still spread over the chip), else 32 (each
-  // workgroup re-reads W_UV[h], so fewer, larger blocks beyond that)
-  const int tb = (size_t)H * ((T + 15) / 16) <= 256 ? 16 : 32;
-  if ((T + tb - 1) / tb > 65535) return MLA_ERR_SHAPE;
+  // token blocks: 32 tokens (two rows per wave) when there are at most 4
+  // parts to hold in flight and more than 256 blocks of 16, else 16; each
+  // workgroup takes as many consecutive blocks of one head (it loads W_UV[h]
+  // once for all of them) as keep at least 256 workgroups, at most 4
+  const int np = P + (local_out ? 1 : 0);
+  const int tb = np <= 4 && (long long)H * ((T + 15) / 16) > 256 ? 32 : 16;
+  const long long nb = (T + tb - 1) / tb;
+  const int nbw = (int)std::max(1LL, std::min(4LL, (long long)H * nb / 256));
+  if ((long long)H * ((nb + nbw - 1) / nbw) > (1LL << 30)) return MLA_ERR_SHAPE;
   const size_t rows = (size_t)T * H;
   const size_t pe = elem_bytes(part_dtype), le = elem_bytes(lse_dtype), e = elem_bytes(dtype);
   Extent ins[5] = {{parts_out, (size_t)P * rows * kDc * pe},
@@ -346,6 +366,7 @@ int mla_combine_vup(const void* parts_out, const void* parts_lse, int P, int par
                     {lse_out, lse_out ? rows * 4 : 0},
                     {lat_out, lat_out ? rows * kDc * e : 0}};
   if (any_overlap(outs, 3, ins, 5)) return MLA_ERR_ALIAS;
+  if (any_misaligned({parts_out, local_out, w_uv, out, lat_out})) return MLA_ERR_RANGE;
   CombineVupParams cv;
   cv.c.parts_out = parts_out;
   cv.c.parts_lse = parts_lse;
@@ -363,6 +384,7 @@ int mla_combine_vup(const void* parts_out, const void* parts_lse, int P, int par
   cv.out = out;
   cv.lat_out = lat_out;
   cv.tb = tb;
+  cv.nbw = nbw;
   return launch_combine_vup(cv, (hipStream_t)stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
@@ -374,6 +396,7 @@ int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype,
   Extent ins[2] = {{x, (size_t)T * H * kDc * e}, {w_uv, (size_t)H * kDc * kDv * e}};
   Extent outs[1] = {{out, (size_t)T * H * kDv * e}};
   if (any_overlap(outs, 1, ins, 2)) return MLA_ERR_ALIAS;
+  if (any_misaligned({x, w_uv, out})) return MLA_ERR_RANGE;
   hipError_t he = dtype == MLA_F32
                     ? launch_vup_simple(x, w_uv, out, T, H, dtype, (hipStream_t)stream)
                     : launch_vup_mfma(x, w_uv, out, T, H, dtype, (hipStream_t)stream);
@@ -389,6 +412,7 @@ int mla_q_absorb(const void* q_nope, const void* w_uk, void* q_lat, int T, int H
   Extent ins[2] = {{q_nope, (size_t)T * H * kDn * e}, {w_uk, (size_t)H * kDc * kDn * e}};
   Extent outs[1] = {{q_lat, (size_t)T * H * kDc * e}};
   if (any_overlap(outs, 1, ins, 2)) return MLA_ERR_ALIAS;
+  if (any_misaligned({q_nope, w_uk, q_lat})) return MLA_ERR_RANGE;
   hipError_t he = dtype == MLA_F32
                     ? launch_absorb_simple(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream)
                     : launch_absorb_mfma(q_nope, w_uk, q_lat, T, H, dtype, (hipStream_t)stream);
@@ -426,6 +450,8 @@ int mla_decode_prologue(const mla_prologue_args* a, void* stream) {
                     {a->kv, cache_rows * kRow * e}};
   // the cache is written in place: check it against every input but itself
   if (any_overlap(outs, 2, ins, 7) || any_overlap(outs + 2, 1, ins, 6)) return MLA_ERR_ALIAS;
+  if (any_misaligned({a->q_nope, a->q_pe, a->w_uk, a->kv_new, a->kv, a->q_lat, a->q_rope}))
+    return MLA_ERR_RANGE;
   PrologueParams pp;
   pp.q_nope = a->q_nope;
   pp.q_pe = a->q_pe;

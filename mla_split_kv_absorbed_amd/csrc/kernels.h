@@ -50,13 +50,16 @@ size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits, int out_
 hipError_t launch_combine(const CombineParams& c, hipStream_t st);
 
 // combine fused with V-up: c.out_dtype is the compute type (bf16 / f16) of
-// w_uv, out and lat_out; tokens per workgroup tb: 16 or 32
+// w_uv, out and lat_out; token blocks of tb = 16 or 32 tokens, nbw (1 .. 4)
+// consecutive blocks of one head per workgroup; H * ceil(ceil(T / tb) / nbw)
+// workgroups must fit in an int
 struct CombineVupParams {
   CombineParams c;
   const void* w_uv;
   void* out;      // [T][H][128]
   void* lat_out;  // [T][H][512] or NULL
   int tb;
+  int nbw;
 };
 hipError_t launch_combine_vup(const CombineVupParams& cv, hipStream_t st);
 hipError_t launch_vup_simple(const void* x, const void* w, void* out, int T, int H, int dt,

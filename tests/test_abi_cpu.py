@@ -81,6 +81,9 @@ def call(a):
     (dict(flags=0x80), -4),
     (dict(out=FAKE), -8), (dict(lse=FAKE + 0x20000000 + 64), -8),
     (dict(workspace=FAKE + 0x50000000), -8),
+    # row tensors must be 16-byte aligned (LSE / int32 arrays need not be)
+    (dict(q_lat=FAKE + 8), -4), (dict(kv=FAKE + 0x20000000 + 4), -4),
+    (dict(out=FAKE + 0x50000000 + 2), -4), (dict(workspace=FAKE + 0x70000000 + 8), -4),
 ])
 def test_partial_validation(over, code):
     assert call(base_args(**over)) == code
@@ -120,6 +123,9 @@ def test_combine_vup_absorb_validation():
     assert lib.mla_q_absorb(FAKE, None, FAKE * 2, 4, 8, 1, None) == -1
     assert lib.mla_q_absorb(FAKE, FAKE * 64, FAKE * 128, 4, 0, 1, None) == -2
     assert lib.mla_q_absorb(FAKE, FAKE * 64, FAKE + 100, 4, 8, 1, None) == -8
+    assert lib.mla_q_absorb(FAKE, FAKE * 64 + 8, FAKE * 128, 4, 8, 1, None) == -4
+    assert lib.mla_vup(FAKE + 4, FAKE * 64, FAKE * 128, 4, 8, 1, None) == -4
+    assert c(FAKE, FAKE * 4, 2, 1, 0, None, None, 4, 8, FAKE * 16 + 8, 1, None, None) == -4
 
 
 def test_fused_combine_vup_validation():
@@ -148,6 +154,9 @@ def test_fused_combine_vup_validation():
     assert call(out=FAKE + 64) == -8           # out overlaps the parts
     assert call(lat=W + 4096) == -8            # merged latent overlaps W_UV
     assert call(lse_out=O + 64) == -8          # the two outputs overlap
+    assert call(w=W + 8) == -4                 # W_UV not 16-byte aligned
+    assert call(out=O + 4) == -4
+    assert call(lat=X + 2) == -4
 
 
 NO_DEVICE = r"""
@@ -159,6 +168,10 @@ print(L.lib().mla_decode_partial(ctypes.byref(base_args()), None))
 print(L.lib().mla_vup(0x10000, 0x20000000, 0x40000000, 4, 8, 1, None))
 print(L.lib().mla_combine_vup(0x10000, 0x400000, 2, 1, 0, None, None, 4, 8, 0x1000000, 1,
                               0x4000000, None, None, None))
+# LSE arrays need only their element alignment: these pass validation too
+print(L.lib().mla_decode_partial(ctypes.byref(base_args(lse=0x10000 + 0x60000000 + 4)), None))
+print(L.lib().mla_combine_vup(0x10000, 0x400002, 2, 1, 1, None, None, 4, 8, 0x1000000, 1,
+                              0x4000000, None, None, None))
 """
 
 
@@ -169,7 +182,7 @@ def test_valid_call_without_device_reports_hip_error():
     r = subprocess.run([sys.executable, "-c", NO_DEVICE % ROOT], capture_output=True, text=True,
                        timeout=300, env=dict(os.environ, HIP_VISIBLE_DEVICES=""))
     assert r.returncode == 0, r.stderr
-    assert r.stdout.split() == ["-7", "-7", "-7"], r.stdout + r.stderr
+    assert r.stdout.split() == ["-7"] * 5, r.stdout + r.stderr
 
 
 def prologue_base(**over):
@@ -200,6 +213,8 @@ def prologue_base(**over):
     (dict(q_lat=FAKE + 0x100), -8),           # q_lat overlaps q_nope
     (dict(q_rope=FAKE + 0x50000000), -8),     # q_rope overlaps the cache
     (dict(kv_new=FAKE + 0x50000040), -8),     # the new rows overlap the cache
+    (dict(q_pe=FAKE + 0x10000002), -4),       # row tensors 16-byte aligned
+    (dict(kv=FAKE + 0x50000008), -4),
 ])
 def test_prologue_validation(over, code):
     a = prologue_base(**over)

@@ -418,9 +418,15 @@ def test_combine(pdt, ldt, local):
 
 @pytest.mark.parametrize("pdt,ldt,dt,n,local,T,H", [
     ("bf16", "bf16", "bf16", 8, False, 32, 128),   # 8 parts, 16-token blocks
-    ("bf16", "f32", "bf16", 4, True, 128, 128),    # history parts + current, 32-token blocks
+    ("bf16", "f32", "bf16", 4, True, 128, 128),    # parts + current: 16-token blocks, 4 per workgroup
     ("f16", "f16", "f16", 2, False, 37, 16),       # ragged last token block
     ("f32", "f32", "bf16", 0, True, 5, 8),         # a local part alone
+    ("f16", "f16", "f16", 2, False, 128, 128),     # 32-token blocks, 2 per workgroup
+    ("bf16", "f32", "bf16", 3, False, 200, 128),   # 32-token blocks, 3 per workgroup, ragged
+    ("f16", "f32", "f16", 5, True, 100, 128),      # 6 parts, 16-token blocks, 3 per workgroup
+    ("f32", "f32", "bf16", 3, False, 70, 128),     # fp32 parts, 32-token blocks
+    ("f32", "f16", "f16", 6, True, 90, 128),       # fp32 parts, 16-token blocks, 3 per workgroup
+    ("bf16", "bf16", "bf16", 10, False, 40, 64),   # more parts than are loaded ahead
 ])
 def test_combine_vup_fused(pdt, ldt, dt, n, local, T, H):
     """mla_combine_vup equals mla_lse_combine (latent in the compute type)
