@@ -147,9 +147,11 @@ __device__ __forceinline__ void merge_issue(const CombineParams& c, const size_t
         const TP* src = k < c.P ? (const TP*)c.parts_out + ((size_t)k * rows + row[r]) * kDc
                                 : (const TP*)c.local_out + row[r] * kDc;
         // the row's address is uniform: kept a scalar base, so only the lane
-        // offset is a vector register (no per-part vector pointers)
+        // offset is a vector register (no per-part vector pointers); the load
+        // is a global one (a flat load would also count against the LDS
+        // counter and hold up the waits for LDS reads)
         asm volatile("" : "+s"(src));
-        ml.raw[r][k] = *(const v8p*)(src + lane * 8);
+        ml.raw[r][k] = *(const __attribute__((address_space(1))) v8p*)(src + lane * 8);
       }
 }
 
