@@ -107,8 +107,9 @@ __device__ __forceinline__ void absorb_block(const T* __restrict__ qn, const T* 
 // loads, every instruction covering whole 256-byte rows (four per
 // instruction), so each cache line is fetched once; the operands are then
 // read from LDS in the matrix layout. Wave w computes c rows 32 w .. of the
-// quarter for every 32-token block of the group, and the results go out
-// through LDS again, one 256-byte row per token. LDS rows are 16 chunks of
+// quarter for every 32-token block of the group; each block's results go out
+// through LDS (the W rows, once every wave holds its own in registers), one
+// 256-byte row per token, as soon as the block is done. LDS rows are 16 chunks of
 // 16 B with chunk c of row r at position c ^ (r & 15), which keeps the
 // operand reads (16 rows per read) free of bank conflicts.
 constexpr int kAbsRows = 128;  // c rows per workgroup
@@ -156,42 +157,39 @@ __global__ __launch_bounds__(256) void absorb_mfma_kernel(const T* __restrict__ 
   for (int k = 0; k < kDn / 16; ++k)
     a[k] = *(const v8*)(wl + (32 * wave + r) * kAbsRowB + abs_pos(2 * k + hi, r));
   const int nblk = (nt + 31) / 32;
-  floatx16 acc[kAbsTok / 32];
+  __syncthreads();  // every wave holds its W rows: their LDS takes the results
+  // Token block bk: its products, then its results (token 32 bk + r, c rows
+  // 32 wave + 8 g + 4 hi .. + 3: 8 bytes at chunk 4 wave + g, half hi of LDS
+  // row 32 bk + r), then one 256-byte row per token to q_lat[t0 + row][h]
+  // [c0 .. c0 + 127]; the stores of a block drain while the next block's
+  // products run.
 #pragma unroll
   for (int bk = 0; bk < kAbsTok / 32; ++bk) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) acc[bk][e] = 0.f;
     if (bk < nblk) {
+      floatx16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
       for (int k = 0; k < kDn / 16; ++k) {
         const v8 b = *(const v8*)(qs + (32 * bk + r) * kAbsRowB + abs_pos(2 * k + hi, r));
-        acc[bk] = GT<T>::mfma(a[k], b, acc[bk]);
+        acc = GT<T>::mfma(a[k], b, acc);
       }
-    }
-  }
-  __syncthreads();  // every wave is done reading W: its rows take the results
-  // result of token 32 bk + r, c rows 32 wave + 8 g + 4 hi .. + 3: 8 bytes at
-  // chunk 4 wave + g, half hi of LDS row 32 bk + r
-#pragma unroll
-  for (int bk = 0; bk < kAbsTok / 32; ++bk) {
-    if (bk < nblk) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         typename GT<T>::v4 v;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = (T)acc[bk][4 * g + e];
+        for (int e = 0; e < 4; ++e) v[e] = (T)acc[4 * g + e];
         *(typename GT<T>::v4*)(wl + (32 * bk + r) * kAbsRowB + abs_pos(4 * wave + g, r) + 8 * hi) = v;
       }
-    }
-  }
-  __syncthreads();
-  // one 256-byte row per token: q_lat[t0 + row][h][c0 .. c0 + 127]
+      __syncthreads();
 #pragma unroll
-  for (int i = 0; i < kAbsTok * 16 / 256; ++i) {
-    const int idx = tid + i * 256, row = idx >> 4, ch = idx & 15;
-    if (row < nt)
-      *(uint4*)(ql + ((size_t)(t0 + row) * H + h) * kDc + c0 + ch * 8) =
-          *(const uint4*)(wl + row * kAbsRowB + abs_pos(ch, row));
+      for (int i = 0; i < 32 * 16 / 256; ++i) {
+        const int idx = tid + i * 256, row = 32 * bk + (idx >> 4), ch = idx & 15;
+        if (row < nt)
+          *(uint4*)(ql + ((size_t)(t0 + row) * H + h) * kDc + c0 + ch * 8) =
+              *(const uint4*)(wl + row * kAbsRowB + abs_pos(ch, row));
+      }
+    }
   }
 }
 
