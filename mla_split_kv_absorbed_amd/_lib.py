@@ -51,6 +51,8 @@ class PartialArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p), ("lse_dtype", ctypes.c_int),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
         ("num_splits", ctypes.c_int), ("flags", ctypes.c_uint),
+        ("plan", ctypes.c_void_p), ("plan_chunks", ctypes.c_int),
+        ("plan_split_units", ctypes.c_int),
     ]
 
 
@@ -116,6 +118,11 @@ def lib():
         L.mla_noalloc_scratch_bytes.argtypes = []
         L.mla_cut_ranges.restype = ci
         L.mla_cut_ranges.argtypes = [i32p, i32p, ci, ci, i32p, i32p]
+        L.mla_decode_partial_plan_words.restype = ctypes.c_size_t
+        L.mla_decode_partial_plan_words.argtypes = [ctypes.POINTER(PartialArgs)]
+        L.mla_decode_partial_make_plan.restype = ci
+        L.mla_decode_partial_make_plan.argtypes = [ctypes.POINTER(PartialArgs), i32p, i32p, i32p,
+                                                   ctypes.c_size_t, ctypes.POINTER(SplitInfo)]
         _lib = L
     return _lib
 
@@ -203,6 +210,28 @@ def mla_decode_partial_plan(a: PartialArgs, range_start, range_end) -> SplitInfo
     _check(lib().mla_decode_partial_plan(ctypes.byref(a), _i32p(rs), _i32p(re_),
                                          ctypes.byref(info)), "mla_decode_partial_plan")
     return info
+
+
+def mla_decode_partial_plan_words(a: PartialArgs) -> int:
+    return lib().mla_decode_partial_plan_words(ctypes.byref(a))
+
+
+def mla_decode_partial_make_plan(a: PartialArgs, range_start, range_end):
+    """The plan mla_decode_partial evaluates on the device, built on the host
+    from host copies of the [P][B] ranges: (int32 numpy table, SplitInfo).
+    The caller copies the table to device memory and sets a.plan,
+    a.plan_chunks = info.chunks, a.plan_split_units = info.split_ranges."""
+    import numpy as np
+    rs, re_ = _host_i32(range_start), _host_i32(range_end)
+    if rs.size != a.P * a.B or re_.size != a.P * a.B:
+        raise ValueError("ranges must hold P x B entries")
+    words = mla_decode_partial_plan_words(a)  # 0: invalid arguments or the plain kernel
+    table = np.zeros(max(words, 1), np.int32)
+    info = SplitInfo()
+    _check(lib().mla_decode_partial_make_plan(ctypes.byref(a), _i32p(rs), _i32p(re_),
+                                              _i32p(table), words, ctypes.byref(info)),
+           "mla_decode_partial_make_plan")
+    return table, info
 
 
 def mla_cut_ranges(range_start, range_end, k: int):

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <vector>
 
 #include "common.h"
 #include "kernels.h"
@@ -85,6 +86,15 @@ int check_partial_args(const mla_partial_args* a) {
   if (!isfinite(a->scale)) return MLA_ERR_RANGE;
   if (a->num_splits < 0 || a->num_splits > 4096) return MLA_ERR_RANGE;
   if (a->flags & ~MLA_FLAG_FORCE_SIMPLE) return MLA_ERR_RANGE;
+  if (a->plan) {
+    // a plan built on the host: only the matrix-core kernel takes one
+    if (!use_mfma(a)) return MLA_ERR_UNSUPPORTED;
+    const long long U = (long long)a->P * a->B;
+    if (a->plan_chunks < 1 || a->plan_chunks > plan_max_chunks(U, a->S, a->num_splits) ||
+        a->plan_split_units < 0 || a->plan_split_units > a->plan_chunks ||
+        a->plan_split_units > U || ((uintptr_t)a->plan & 15))
+      return MLA_ERR_RANGE;
+  }
   return MLA_OK;
 }
 
@@ -93,16 +103,19 @@ int check_partial_alias(const mla_partial_args* a, size_t ws) {
   const size_t e = elem_bytes(a->q_dtype);
   const size_t kv_rows = a->block_size > 0 ? (size_t)a->num_blocks * a->block_size
                                            : (size_t)a->B * a->kv_seq_stride;
-  Extent ins[6] = {{a->q_lat, T * H * kDc * e},
+  Extent ins[7] = {{a->q_lat, T * H * kDc * e},
                    {a->q_rope, T * H * kDr * e},
                    {a->kv, kv_rows * kRow * e},
                    {a->block_table, a->block_table ? (size_t)a->B * a->max_blocks * 4 : 0},
                    {a->range_start, P * a->B * 4},
-                   {a->range_end, P * a->B * 4}};
+                   {a->range_end, P * a->B * 4},
+                   {a->plan, a->plan ? (size_t)plan_table_words((long long)P * a->B, a->S,
+                                                                a->num_splits) * 4
+                                     : 0}};
   Extent outs[3] = {{a->out, P * T * H * kDc * elem_bytes(a->out_dtype)},
                     {a->lse, P * T * H * elem_bytes(a->lse_dtype)},
                     {a->workspace, ws}};
-  if (any_overlap(outs, 3, ins, 6)) return MLA_ERR_ALIAS;
+  if (any_overlap(outs, 3, ins, 7)) return MLA_ERR_ALIAS;
   if (any_misaligned({a->q_lat, a->q_rope, a->kv, a->out, ws ? a->workspace : nullptr}))
     return MLA_ERR_RANGE;
   return MLA_OK;
@@ -112,7 +125,7 @@ int check_partial_alias(const mla_partial_args* a, size_t ws) {
 
 extern "C" {
 
-int mla_abi_version(void) { return 1; }
+int mla_abi_version(void) { return 2; }
 
 const char* mla_status_string(int s) {
   switch (s) {
@@ -182,6 +195,9 @@ int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_by
   pp.out_dtype = a->out_dtype;
   pp.lse_dtype = a->lse_dtype;
   pp.num_splits = a->num_splits;
+  pp.plan = a->plan;
+  pp.plan_chunks = a->plan_chunks;
+  pp.plan_split_units = a->plan_split_units;
   pp.scale = a->scale;
   pp.capacity = a->block_size > 0 ? (long long)a->max_blocks * a->block_size
                                   : (long long)a->kv_seq_stride;
@@ -269,6 +285,112 @@ int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_star
   info->equal_splits = equal && U > 0 ? unit_chunks(nt0, c_auto, 0) : 0;
   info->max_chunks = (int)plan_max_chunks(U, a->S, hint);
   info->max_split_slots = (int)plan_max_split_slots(U, a->S, hint);
+  return MLA_OK;
+}
+
+size_t mla_decode_partial_plan_words(const mla_partial_args* a) {
+  if (!a) return 0;
+  mla_partial_args c = *a;
+  c.plan = nullptr;  // the size of a plan does not depend on one being set
+  if (check_partial_args(&c) != MLA_OK || !use_mfma(&c)) return 0;
+  return (size_t)plan_table_words((long long)c.P * c.B, c.S, c.num_splits);
+}
+
+int mla_decode_partial_make_plan(const mla_partial_args* a, const int32_t* range_start,
+                                 const int32_t* range_end, int32_t* plan, size_t plan_words,
+                                 mla_split_info* info) {
+  if (!a) return MLA_ERR_NULL;
+  mla_partial_args c = *a;
+  c.plan = nullptr;
+  int st = check_partial_args(&c);
+  if (st != MLA_OK) return st;
+  if (!range_start || !range_end || !plan || !info) return MLA_ERR_NULL;
+  if (!use_mfma(&c)) return MLA_ERR_UNSUPPORTED;
+  const long long U = (long long)c.P * c.B;
+  const int S = c.S, hint = c.num_splits;
+  const long long words = plan_table_words(U, S, hint);
+  if ((long long)plan_words < words) return MLA_ERR_WORKSPACE;
+  st = mla_decode_partial_plan(&c, range_start, range_end, info);
+  if (st != MLA_OK) return st;
+  const long long capacity =
+      c.block_size > 0 ? (long long)c.max_blocks * c.block_size : (long long)c.kv_seq_stride;
+  std::vector<int> nt((size_t)U);
+  for (long long u = 0; u < U; ++u) {
+    const int s0 = range_start[u], e0 = range_end[u];
+    nt[u] = range_bad(s0, e0, capacity) ? 0 : range_tiles(s0, e0);
+  }
+  memset(plan, 0, (size_t)words * 4);
+  plan[0] = kPlanMagic;
+  plan[1] = info->chunks;
+  plan[2] = info->split_ranges;
+  plan[3] = info->chunk_tiles;
+  plan[4] = (int)U;
+  plan[5] = S;
+  plan[6] = hint;
+  int32_t* ent = plan + kPlanHeader;
+  int32_t* desc = plan + plan_desc_offset(U, S, hint);
+  auto put = [&](long long id, long long u, int tb, int te, long long slot) {
+    int32_t* e = ent + id * kPlanEntry;
+    e[0] = (int)u;
+    e[1] = tb;
+    e[2] = te;
+    e[3] = (int)slot;
+  };
+  if (hint > 0) {
+    // the explicit count: chunk id -> (range, piece) as the device maps it,
+    // the k pieces of a range on one XCD when the range count is a multiple of 8
+    const int k = hint;
+    for (long long id = 0; id < U * k; ++id) {
+      long long u, i;
+      if ((U & 7) == 0) {
+        const long long pos = id >> 3;
+        u = (id & 7) + 8 * (pos / k);
+        i = pos % k;
+      } else {
+        u = id / k;
+        i = id % k;
+      }
+      put(id, u, piece_tile((int)i, nt[u], k), piece_tile((int)i + 1, nt[u], k),
+          k > 1 ? u * k + i : -1);
+    }
+    if (k > 1)
+      for (long long u = 0; u < U; ++u) {
+        desc[u * kPlanDesc + 0] = (int)u;
+        desc[u * kPlanDesc + 1] = (int)(u * k);
+        desc[u * kPlanDesc + 2] = k;
+      }
+    return MLA_OK;
+  }
+  // the automatic plan: chunk ids longest first by bucket, range order within a
+  // bucket; slots and split indices in range order
+  const int cs = info->chunk_tiles;
+  std::vector<int> n((size_t)U), bucket((size_t)U);
+  long long tot[kBuckets] = {0};
+  for (long long u = 0; u < U; ++u) {
+    n[u] = unit_chunks(nt[u], cs, 0);
+    bucket[u] = len_bucket((nt[u] + n[u] - 1) / n[u], cs);
+    tot[bucket[u]] += n[u];
+  }
+  long long run[kBuckets];
+  for (int b = 0; b < kBuckets; ++b) {
+    run[b] = 0;
+    for (int b2 = b + 1; b2 < kBuckets; ++b2) run[b] += tot[b2];
+  }
+  long long soff = 0, poff = 0;
+  for (long long u = 0; u < U; ++u) {
+    const long long off = run[bucket[u]];
+    run[bucket[u]] += n[u];
+    for (int k = 0; k < n[u]; ++k)
+      put(off + k, u, piece_tile(k, nt[u], n[u]), piece_tile(k + 1, nt[u], n[u]),
+          n[u] > 1 ? soff + k : -1);
+    if (n[u] > 1) {
+      desc[poff * kPlanDesc + 0] = (int)u;
+      desc[poff * kPlanDesc + 1] = (int)soff;
+      desc[poff * kPlanDesc + 2] = n[u];
+      soff += n[u];
+      poff += 1;
+    }
+  }
   return MLA_OK;
 }
 

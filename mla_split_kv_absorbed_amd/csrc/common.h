@@ -73,6 +73,8 @@ struct PartialParams {
   int out_dtype, lse_dtype;
   int num_splits;   // 0 = automatic
   int max_chunks;   // grid bound of the main kernel (in chunks)
+  const int32_t* plan;  // a plan built on the host (plan.h layout), or NULL
+  int plan_chunks, plan_split_units;  // its chunk and cut-range counts
   float scale;
   long long capacity;  // tokens addressable per sequence
 };

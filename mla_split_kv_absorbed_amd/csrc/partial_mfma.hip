@@ -256,19 +256,9 @@ struct Found {
 // units per thread whose ranges stay in registers through the plan
 constexpr int kPlanCache = 4;
 
-// Chunk ids are handed out longest chunks first: chunks fall into 8 length
-// buckets of the chunk size, bucket by bucket from the longest, in unit order
-// within a bucket (one block scan, the same order in every workgroup), so
-// the in-order dispatch of workgroups places long chunks early on ragged
-// batches.
-constexpr int kBuckets = 8;
-
-__device__ __forceinline__ int len_bucket(int len, int c) {
-  // len <= c + 1 < 2^27 tiles, so 8 len fits in 32 bits; a uniform bucket
-  // set (equal chunks) skips the division
-  return len >= c ? kBuckets - 1 : min(kBuckets - 1, (unsigned)len * kBuckets / (unsigned)(c + 1));
-}
-
+// The automatic plan on the device, by the whole workgroup (block scans over
+// the ranges; chunk ids longest first by the buckets of plan.h, range order
+// within a bucket; slots and split indices in range order).
 __device__ __forceinline__ Plan make_plan(const PartialParams& pp, int want, Found* found, int* sh) {
   const int tid = threadIdx.x;
   const int U = pp.P * pp.B;
@@ -465,7 +455,32 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   }
   Found fd;
   bool first;  // this piece is the first of its range
-  if (pp.num_splits > 0) {
+  if (pp.plan) {
+    // A plan built on the host: this chunk's entry. Every field is checked
+    // against the arguments (the range is read from the range arrays, the
+    // tiles clamped to it, the slot to the workspace), so a table that does
+    // not belong to them gives wrong results but no access out of bounds.
+    if (chunk >= pp.plan_chunks) return;  // grid slack
+    const int* e = pp.plan + kPlanHeader + (size_t)chunk * kPlanEntry;
+    const int u = __builtin_amdgcn_readfirstlane(e[0]);
+    if (u < 0 || u >= pp.P * pp.B) return;
+    const Unit x = load_unit(pp, u);
+    const int tb = min(max(__builtin_amdgcn_readfirstlane(e[1]), 0), x.nt);
+    const int te = min(max(__builtin_amdgcn_readfirstlane(e[2]), tb), x.nt);
+    int slot = __builtin_amdgcn_readfirstlane(e[3]);
+    if (slot < 0 || slot >= plan_max_split_slots((long long)pp.P * pp.B, S, pp.num_splits))
+      slot = -1;
+    fd.u = u;
+    fd.tb = tb;
+    fd.te = te;
+    fd.slot = slot;
+    fd.nsplit = 0;
+    fd.split_idx = -1;  // the cut ranges' descriptors are in the plan
+    fd.st = x.st;
+    fd.en = x.en;
+    first = false;
+    __syncthreads();
+  } else if (pp.num_splits > 0) {
     // An explicit count k: every range is cut into exactly k chunks (some
     // may be empty), so the plan has a closed form and its scans are
     // skipped. Chunk i of range u covers tiles [i nt / k, (i + 1) nt / k) of
@@ -1109,7 +1124,12 @@ template <typename TO>
 __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
   const int lane = threadIdx.x & 63;
-  const int n_units = *mp.ws_count;
+  // (a plan built on the host supplies the count and the descriptors: both
+  // are checked, so a table that does not belong to the arguments stays in
+  // bounds)
+  const int U = pp.P * pp.B;
+  const int n_units = min(max(*mp.ws_count, 0), U);
+  const long long slots = plan_max_split_slots(U, pp.S, pp.num_splits);
   const long long rows = (long long)n_units * pp.S * pp.H;
   const int Tq = pp.B * pp.S;
   const long long waves = (long long)gridDim.x * 4;
@@ -1119,6 +1139,7 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
     const int k = (int)(r / ((long long)pp.H * pp.S));
     const intx4 dsc = mp.ws_desc[k];
     const int u = dsc[0], slot0 = dsc[1], n = dsc[2];
+    if (u < 0 || u >= U || slot0 < 0 || n < 1 || (long long)slot0 + n > slots) continue;
     auto wrow = [&](int i) { return ((size_t)(slot0 + i) * pp.S + s) * pp.H + h; };
     float m = -INFINITY;
     bool nan_seen = false;
@@ -1198,7 +1219,15 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
   mp.ws_desc = (intx4*)(ws + w.desc_off);
   mp.pp.ws_lse = (float*)(ws + w.lse_off);
   mp.pp.ws_out = ws + w.out_off;
-  const size_t chunks = mfma_max_chunks(pp_in.B, pp_in.S, pp_in.P, pp_in.num_splits);
+  const long long U = (long long)pp_in.P * pp_in.B;
+  if (pp_in.plan) {
+    // the plan's cut-range count and descriptors (read-only to the merge)
+    mp.ws_count = const_cast<int*>(pp_in.plan + 2);
+    mp.ws_desc = (intx4*)const_cast<int*>(
+        pp_in.plan + plan_desc_offset(U, pp_in.S, pp_in.num_splits));
+  }
+  const size_t chunks = pp_in.plan ? (size_t)pp_in.plan_chunks
+                                   : mfma_max_chunks(pp_in.B, pp_in.S, pp_in.P, pp_in.num_splits);
   size_t groups = chunks * pp_in.S;
   if (pp_in.S > 1) groups = (groups + 8 * pp_in.S - 1) / (8 * pp_in.S) * (8 * pp_in.S);
   // blockIdx.y: the group of 128 heads
@@ -1217,13 +1246,14 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // no sub-splits requested: every range is written directly, nothing to merge
-  if (pp_in.num_splits == 1) return hipSuccess;
+  // no sub-splits requested (or none in the host's plan): every range is
+  // written directly, nothing to merge
+  if (pp_in.num_splits == 1 || (pp_in.plan && pp_in.plan_split_units == 0)) return hipSuccess;
   // one wave per merged row: at most min(U, groups) split units (a split
   // unit has more tiles than a chunk), capped; the kernel strides beyond
-  const size_t split_units = pp_in.num_splits > 1
-                                 ? (size_t)pp_in.P * pp_in.B
-                                 : std::min((size_t)pp_in.P * pp_in.B, (size_t)kTargetGroups);
+  const size_t split_units = pp_in.plan            ? (size_t)pp_in.plan_split_units
+                             : pp_in.num_splits > 1 ? (size_t)U
+                                                    : std::min((size_t)U, (size_t)kTargetGroups);
   const size_t merge_rows = split_units * pp_in.S * pp_in.H;
   const unsigned merge_blocks = (unsigned)std::max<size_t>(
       1, std::min<size_t>((merge_rows + 3) / 4, 2048));

@@ -89,4 +89,39 @@ __host__ __device__ inline long long plan_max_split_slots(long long U, int S, in
   return (2LL * kTargetGroups + S - 1) / S + 1;
 }
 
+// The automatic plan hands out chunk ids longest chunks first: chunks fall
+// into kBuckets length buckets of the chunk size, bucket by bucket from the
+// longest, in range order within a bucket, so the in-order dispatch of
+// workgroups places long chunks early on ragged batches. A range of nt tiles
+// in n chunks is in bucket len_bucket(ceil(nt / n), c).
+constexpr int kBuckets = 8;
+
+__host__ __device__ inline int len_bucket(int len, int c) {
+  // len <= c + 1 < 2^27 tiles, so kBuckets len fits in 32 bits
+  if (len >= c) return kBuckets - 1;
+  const int b = (int)((unsigned)len * kBuckets / (unsigned)(c + 1));
+  return b < kBuckets - 1 ? b : kBuckets - 1;
+}
+
+// A plan built on the host (mla_decode_partial_make_plan), int32 words:
+//   header, kPlanHeader words: kPlanMagic, chunks, cut ranges, chunk tiles,
+//     ranges U, queries S, num_splits, 0
+//   at kPlanHeader: plan_max_chunks entries of kPlanEntry words, one per
+//     chunk id: range, first tile, end tile, slot of its result (-1: the
+//     part output), 0, 0, 0, 0
+//   at plan_desc_offset: U descriptors of kPlanDesc words, one per cut range
+//     in range order: range, first slot, pieces, 0
+constexpr int kPlanMagic = 0x4D4C4131;
+constexpr int kPlanHeader = 8;
+constexpr int kPlanEntry = 8;
+constexpr int kPlanDesc = 4;
+
+__host__ __device__ inline long long plan_desc_offset(long long U, int S, int hint) {
+  return kPlanHeader + kPlanEntry * plan_max_chunks(U, S, hint);
+}
+
+__host__ __device__ inline long long plan_table_words(long long U, int S, int hint) {
+  return plan_desc_offset(U, S, hint) + kPlanDesc * U;
+}
+
 }  // namespace mla

@@ -32,10 +32,15 @@ class DecodeStep:
     def __init__(self, w: Workload, device="cuda", part_lse_dtype: Optional[str] = None,
                  num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None,
                  side_stream: bool = False, fused_tail: bool = True, keep_latent: bool = False,
-                 host_subranges: bool = False, auto_plan: bool = False):
+                 host_subranges: bool = False, auto_plan: bool = False,
+                 host_plan: bool = False):
         """num_splits: 0 lets the library plan; for equal ranges the plan's
         chunk count is then passed explicitly (the kernel skips its plan)
         unless auto_plan is set.
+        host_plan: when the history call runs the automatic plan (ragged
+        ranges, or auto_plan), the plan is built on the host from the ranges
+        (mla_decode_partial_make_plan) and handed to the call in device
+        memory, as a serving loop that holds its sequence lengths would.
         host_subranges: a single part without a current chunk, whose
         ranges the partial call would cut into k > 1 sub-ranges (equal ranges,
         bf16 / fp16), is instead cut on the host (cut_ranges) and passed as k
@@ -116,6 +121,14 @@ class DecodeStep:
         for a in [self.hist_args] + ([self.cur_args] if sp.current else []):
             a.workspace = self.workspace.data_ptr()
             a.workspace_bytes = self.workspace.numel()
+        self.plan = None
+        if (host_plan and self.hist_args.num_splits == 0
+                and L.mla_decode_partial_plan_words(self.hist_args) > 0):
+            table, info = L.mla_decode_partial_make_plan(self.hist_args, rs, re_)
+            self.plan = torch.from_numpy(table).to(dev)
+            self.hist_args.plan = self.plan.data_ptr()
+            self.hist_args.plan_chunks = info.chunks
+            self.hist_args.plan_split_units = info.split_ranges
         # Current-chunk attention on a side stream, concurrent with the
         # history partial (the study page's stream split). It gets its own
         # workspace: a workspace belongs to one call until its stream has

@@ -41,7 +41,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert L.mla_abi_version() == 1
+    assert L.mla_abi_version() == 2
     for code, name in L.STATUS.items():
         assert L.mla_status_string(code).startswith(name)
     assert L.mla_status_string(12345) == "unknown status"
