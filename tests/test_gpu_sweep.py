@@ -2,8 +2,8 @@
 partial call, each against the float64 oracle: batch sizes, head counts,
 query lengths, block sizes (paged 32 / 64 / 128 and contiguous), part
 counts, explicit and automatic split counts, ragged and empty ranges, and
-the three storage types. Sizes stay small enough for the oracle to finish
-in seconds per case."""
+the three storage types; every other case with the split plan built on the
+host. Sizes stay small enough for the oracle to finish in seconds per case."""
 import numpy as np
 import pytest
 import torch
@@ -45,8 +45,9 @@ def test_sweep_step_and_partial(i):
     sp = W.spec(wid, **over)
     say(f"[sweep {i}] {over} splits={splits}")
     w = W.make_workload(sp)
-    # the whole step (absorb, partial over the parts [+ current], combine, V-up)
-    st = DecodeStep(w, num_splits=splits, auto_plan=splits == 0)
+    # the whole step (absorb, partial over the parts [+ current], combine, V-up);
+    # every other case hands the partial call a plan built on the host
+    st = DecodeStep(w, num_splits=splits, auto_plan=splits == 0, host_plan=i % 2 == 0)
     st.run()
     torch.cuda.synchronize()
     extra = sp.part_lse_dtype if sp.part_lse_dtype != "f32" else None
