@@ -1109,19 +1109,13 @@ __device__ __forceinline__ void store8(TO* dst, const float* v) {
   *(v8o*)dst = x;
 }
 
-// 8 consecutive values of a partial row stored in the output type
-template <typename TO>
-__device__ __forceinline__ void load8(const TO* src, float* v) {
-  typedef TO v8o __attribute__((ext_vector_type(8)));
-  const v8o x = *(const v8o*)src;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = (float)x[i];
-}
-
 // Lane i holds the LSE of chunk i0 + i; the chunks' partial rows (in the
 // output type TO) are then accumulated in ascending order, 4 rows in flight.
+// The first 64 LSEs and the first 4 rows are requested together, so a range
+// of up to 4 pieces costs one round trip before its store.
 template <typename TO>
 __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
+  typedef TO v8o __attribute__((ext_vector_type(8)));
   const PartialParams& pp = mp.pp;
   const int lane = threadIdx.x & 63;
   // (a plan built on the host supplies the count and the descriptors: both
@@ -1141,9 +1135,15 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
     const int u = dsc[0], slot0 = dsc[1], n = dsc[2];
     if (u < 0 || u >= U || slot0 < 0 || n < 1 || (long long)slot0 + n > slots) continue;
     auto wrow = [&](int i) { return ((size_t)(slot0 + i) * pp.S + s) * pp.H + h; };
-    float m = -INFINITY;
-    bool nan_seen = false;
-    for (int i0 = 0; i0 < n; i0 += 64) {
+    auto row_ptr = [&](int i) { return (const v8o*)((const TO*)pp.ws_out + wrow(i) * kDc) + lane; };
+    const float l0 = lane < n ? pp.ws_lse[wrow(lane)] : -INFINITY;
+    v8o raw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < n) raw[q] = *row_ptr(q);
+    bool nan_seen = isnan(l0);
+    float m = l0;
+    for (int i0 = 64; i0 < n; i0 += 64) {
       const float li = i0 + lane < n ? pp.ws_lse[wrow(i0 + lane)] : -INFINITY;
       nan_seen |= isnan(li);
       m = fmaxf(m, li);
@@ -1155,21 +1155,22 @@ __global__ __launch_bounds__(256) void split_merge_kernel(MfmaParams mp) {
     if (m != -INFINITY && !nan_seen) {
       for (int i0 = 0; i0 < n; i0 += 64) {
         const int cnt = min(64, n - i0);
-        const float li = lane < cnt ? pp.ws_lse[wrow(i0 + lane)] : -INFINITY;
+        const float li =
+            i0 == 0 ? l0 : (lane < cnt ? pp.ws_lse[wrow(i0 + lane)] : -INFINITY);
         const float wl = li == -INFINITY ? 0.f : expf(li - m);
         z += wave_sum(wl);
         for (int i = 0; i < cnt; i += 4) {
-          float a[4][8];
+          if (i0 + i > 0) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (i + q < cnt)
-              load8<TO>((const TO*)pp.ws_out + wrow(i0 + i + q) * kDc + lane * 8, a[q]);
+            for (int q = 0; q < 4; ++q)
+              if (i + q < cnt) raw[q] = *row_ptr(i0 + i + q);
+          }
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float w = __shfl(wl, i + q, 64);
             if (i + q < cnt && w != 0.f)
 #pragma unroll
-              for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, a[q][e], acc[e]);
+              for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)raw[q][e], acc[e]);
           }
         }
       }
