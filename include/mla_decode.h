@@ -134,8 +134,8 @@ enum {
  *   mla_split_info), outside [1, max_chunks] / [0, min(P B, plan_chunks)]
  *   MLA_ERR_RANGE. A plan made for other arguments or ranges gives wrong
  *   results but never an access out of bounds (every entry is checked on the
- *   device against the range arrays and the workspace). The plain kernel
- *   takes none (MLA_ERR_UNSUPPORTED).
+ *   device against the range arrays and the workspace). The plain and the
+ *   short-range kernels take none (MLA_ERR_UNSUPPORTED).
  */
 typedef struct mla_partial_args {
   const void* q_lat;
@@ -170,9 +170,13 @@ typedef struct mla_partial_args {
 /* How mla_decode_partial divides its work (the split rule it evaluates on
  * the device from the range arrays), reported by mla_decode_partial_plan. */
 typedef struct mla_split_info {
-  int matrix_path;     /* 1: the matrix-core kernel (bf16 / fp16); 0: the plain
-                          kernel (fp32, or MLA_FLAG_FORCE_SIMPLE), which runs one
-                          workgroup per (range, query, head) and cuts nothing */
+  int matrix_path;     /* 1: the matrix-core kernel (bf16 / fp16); 2: the
+                          short-range kernel (bf16 / fp16 over a contiguous
+                          cache with kv_seq_stride <= 8), one wave per (range,
+                          query) and 4 heads; 0: the plain kernel (fp32, or
+                          MLA_FLAG_FORCE_SIMPLE), one workgroup per (range,
+                          query, head). Paths 0 and 2 cut nothing, need no
+                          workspace and take no plan. */
   int chunk_tiles;     /* tiles of 32 keys per chunk of the automatic plan
                           (num_splits == 0); 0 with an explicit num_splits */
   int chunks;          /* chunks: each runs as one workgroup per query token
@@ -208,7 +212,7 @@ int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_star
 
 /* int32 words of a plan for these arguments (a pure function of P, B, S and
  * num_splits; `a->plan` is ignored); 0 for invalid arguments or the plain
- * kernel. */
+ * and short-range kernels. */
 size_t mla_decode_partial_plan_words(const mla_partial_args* a);
 
 /* Builds on the host the plan mla_decode_partial would evaluate on the
@@ -245,9 +249,13 @@ size_t mla_decode_partial_workspace_size(const mla_partial_args* a);
  * the HISTORY and CURRENT attention calls, each returning output + LSE).
  * bf16 / fp16 run on the matrix-core kernel for any H, in groups of 128
  * heads that each read the part's keys once (a group with fewer real heads
- * computes the missing rows from zero queries and never stores them); fp32
- * (and MLA_FLAG_FORCE_SIMPLE) runs on the plain kernel, one workgroup per
- * (part, query, head). S <= 64 (MLA_ERR_UNSUPPORTED above).
+ * computes the missing rows from zero queries and never stores them), except
+ * over a contiguous cache with kv_seq_stride <= 8 (no valid range then holds
+ * more than 8 keys: the study page's CURRENT call over the q_len tokens of
+ * the chunk), which runs on a vector kernel of one wave per (part, query)
+ * and 4 heads with an exact fp32 softmax; fp32 (and MLA_FLAG_FORCE_SIMPLE)
+ * runs on the plain kernel, one workgroup per (part, query, head). S <= 64
+ * (MLA_ERR_UNSUPPORTED above).
  * Softmax range (K3 page, section 4.2: the online-softmax rescale is
  * mandatory): the matrix kernel exponentiates relative to a per-chunk
  * reference (bf16: 0, head maxima within +-64 in log2 units; fp16: each

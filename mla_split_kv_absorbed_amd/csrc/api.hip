@@ -50,8 +50,16 @@ bool any_misaligned(std::initializer_list<const void*> ps) {
   return false;
 }
 
-bool use_mfma(const mla_partial_args* a) {
+// bf16 / fp16 over a contiguous cache of at most kShortKeys keys per
+// sequence (the current-chunk call): the short-range kernel
+bool use_short(const mla_partial_args* a) {
   return !(a->flags & MLA_FLAG_FORCE_SIMPLE) &&
+         (a->q_dtype == MLA_BF16 || a->q_dtype == MLA_F16) && a->block_size == 0 &&
+         a->kv_seq_stride <= kShortKeys;
+}
+
+bool use_mfma(const mla_partial_args* a) {
+  return !(a->flags & MLA_FLAG_FORCE_SIMPLE) && !use_short(a) &&
          mfma_path_supported(a->q_dtype, a->H, a->block_size);
 }
 
@@ -203,7 +211,9 @@ int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_by
                                   : (long long)a->kv_seq_stride;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (use_mfma(a)) {
+  if (use_short(a)) {
+    e = launch_partial_short(pp, a->q_dtype, s);
+  } else if (use_mfma(a)) {
     pp.ws_out = workspace;  // workspace base; the launcher lays it out
     pp.max_chunks = (int)mfma_max_chunks(a->B, a->S, a->P, a->num_splits);
     e = launch_partial_mfma(pp, a->q_dtype, s);
@@ -226,9 +236,10 @@ int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_star
                                                : (long long)a->kv_seq_stride;
   const long long U = (long long)a->P * a->B;
   memset(info, 0, sizeof(*info));
-  info->matrix_path = use_mfma(a) ? 1 : 0;
-  if (!info->matrix_path) {
-    // the plain kernel: one workgroup per (range, query, head), no chunks
+  info->matrix_path = use_mfma(a) ? 1 : use_short(a) ? 2 : 0;
+  if (info->matrix_path != 1) {
+    // the plain and the short-range kernels: one workgroup / wave per
+    // (range, query, head), no chunks
     info->chunks = (int)U;
     return MLA_OK;
   }

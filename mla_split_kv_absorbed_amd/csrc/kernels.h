@@ -40,6 +40,12 @@ int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_by
 size_t partial_workspace_need(const mla_partial_args* a);
 
 hipError_t launch_partial_simple(const PartialParams& pp, int dtype, hipStream_t st);
+// Short ranges: a contiguous cache (block_size 0) with kv_seq_stride <=
+// kShortKeys bounds every valid range by kShortKeys keys; bf16 / fp16 calls
+// of that shape run on a vector kernel of one wave per (part, query, head)
+// row instead of the matrix kernel.
+constexpr int kShortKeys = 8;
+hipError_t launch_partial_short(const PartialParams& pp, int dtype, hipStream_t st);
 // MFMA path: q/kv dtype bf16 or f16, H % 128 == 0, block_size % 32 == 0 (or contiguous).
 bool mfma_path_supported(int dtype, int H, int block_size);
 hipError_t launch_partial_mfma(const PartialParams& pp, int dtype, hipStream_t st);

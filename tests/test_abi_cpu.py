@@ -235,3 +235,24 @@ def test_noalloc_rejects_before_any_device_call():
     need = lib.mla_decode_partial_workspace_size(ctypes.byref(a))
     assert need > 96 << 20
     assert lib.mla_decode_partial_noalloc(ctypes.byref(a), None) == -5
+
+
+@pytest.mark.parametrize("dtype,stride,flags,path", [
+    (L.MLA_BF16, 2, 0, 2), (L.MLA_F16, 8, 0, 2),   # short ranges: the vector kernel
+    (L.MLA_BF16, 9, 0, 1), (L.MLA_F16, 64, 0, 1),  # longer: the matrix kernel
+    (L.MLA_BF16, 2, L.MLA_FLAG_FORCE_SIMPLE, 0), (L.MLA_F32, 2, 0, 0),
+])
+def test_contiguous_short_range_routing(dtype, stride, flags, path):
+    """A bf16 / fp16 call over a contiguous cache of at most 8 keys per
+    sequence takes the short-range kernel (matrix_path 2): it needs no
+    workspace and takes no host plan; longer strides keep the matrix kernel."""
+    a = base_args(block_size=0, block_table=None, kv_seq_stride=stride, q_dtype=dtype,
+                  kv_dtype=dtype, out_dtype=dtype, flags=flags)
+    rs = [0] * (a.P * a.B)
+    info = L.mla_decode_partial_plan(a, rs, [stride] * (a.P * a.B))
+    assert info.matrix_path == path
+    assert (L.mla_decode_partial_workspace_size(a) == 0) == (path != 1)
+    assert (L.mla_decode_partial_plan_words(a) == 0) == (path != 1)
+    if path != 1:
+        a.plan, a.plan_chunks = FAKE + 0x48000000, 1
+        assert call(a) == -6  # MLA_ERR_UNSUPPORTED
