@@ -29,13 +29,16 @@ HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20   # MI355X Infinity Cache
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 KERNEL_SRCS = [os.path.join(ROOT, "mla_split_kv_absorbed_amd", "csrc", f)
-               for f in ("partial_mfma.hip", "common.h", "kernels.h", "plan.h")]
+               for f in ("partial_mfma.hip", "common.h", "kernels.h", "plan.h", "short.h")]
 PMC_FILE = os.path.join(ROOT, "profiles", "partial_mfma_kernel_pmc.json")
 # how the timed decode step is built (the full-size parity tests build theirs
 # the same way): a single part's sub-ranges are cut on the host and merged by
 # the fused combine + V-up; a ragged batch's split plan is built on the host
-# with the other metadata (before the timed region, as the ranges are)
-BENCH_STEP_OPTS = {"host_subranges": True, "host_plan": True}
+# with the other metadata (before the timed region, as the ranges are); the
+# MTP workload's current chunk runs in the history call's launch
+# (mla_decode_partial_pair: its workgroups fill the end of the history's
+# schedule)
+BENCH_STEP_OPTS = {"host_subranges": True, "host_plan": True, "pair_current": True}
 
 
 def kernel_hash(srcs=None) -> str:
@@ -116,8 +119,8 @@ def pmc_summary(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, commands):
         "kernel": "partial_mfma_kernel<bf16>",
         "workload": "config2:bf16_B32_H128_L32768_paged32_8parts",
         "kernel_sha": kernel_hash(),
-        "kernel_sha_of": "bench.kernel_hash(): partial_mfma.hip, common.h, kernels.h and plan.h "
-                         "with comments and blank lines dropped",
+        "kernel_sha_of": "bench.kernel_hash(): partial_mfma.hip, common.h, kernels.h, plan.h "
+                         "and short.h with comments and blank lines dropped",
         "fetch_kib_per_dispatch": round(fetch, 3),
         "write_kib_per_dispatch": round(write, 3),
         "dispatches": {"fetch": nf, "write": nw},
@@ -412,9 +415,12 @@ def main():
         if st.absorb:
             L.mla_q_absorb(st.q_nope, st.w_uk, st.q_lat, stream)
         ev[i][0].record(stream)
-        L.mla_decode_partial(st.hist_args, stream)
+        if st.pair:
+            L.mla_decode_partial_pair(st.hist_args, st.cur_args, stream)
+        else:
+            L.mla_decode_partial(st.hist_args, stream)
         ev[i][1].record(stream)
-        if sp.current:
+        if sp.current and not st.pair:
             L.mla_decode_partial(st.cur_args, stream)
         if st.fused_tail:
             L.mla_combine_vup(st.parts_out, st.parts_lse, st.w_uv, st.out, st.lse,
@@ -517,7 +523,9 @@ def main():
                           "frac": round(t_roof * 1e6 / us, 4),
                           "algorithmic_bytes": work["total_bytes"],
                           "algorithmic_flops": work["total_flops"]},
-        "roofline": {"kernel": "partial_mfma_kernel (mla_decode_partial, all parts)",
+        "roofline": {"kernel": ("partial_mfma_kernel (mla_decode_partial_pair: all history "
+                                "parts + the current chunk)" if st.pair else
+                                "partial_mfma_kernel (mla_decode_partial, all parts)"),
                      "bound": "mfma" if part_mfma else "hbm", "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "bytes_per_launch": part_bytes,

@@ -265,6 +265,21 @@ size_t mla_decode_partial_workspace_size(const mla_partial_args* a);
  * window. Any finite scores give finite results. */
 int mla_decode_partial(const mla_partial_args* a, void* stream);
 
+/* The HISTORY and CURRENT partial calls of one decode step in one launch
+ * (study page, design section: the current chunk's attention runs while the
+ * history's does; here both share one grid instead of two streams). `hist`
+ * must take the matrix-core kernel (bf16 / fp16) and `cur` the short-range
+ * kernel (same dtype, contiguous cache with kv_seq_stride <= 8), else
+ * MLA_ERR_UNSUPPORTED; each is validated as by mla_decode_partial (hist
+ * with its own workspace and optional plan). The current call's workgroups
+ * come after the history's chunks in dispatch order, so they run on the
+ * compute units the history's schedule frees at its end. Neither call's
+ * outputs (or hist's workspace) may overlap anything the other reads or
+ * writes (MLA_ERR_ALIAS); reading the same queries is allowed. Outputs are
+ * bitwise those of the two separate calls. */
+int mla_decode_partial_pair(const mla_partial_args* hist, const mla_partial_args* cur,
+                            void* stream);
+
 /* mla_decode_partial without a caller workspace, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc). It runs the same kernels with

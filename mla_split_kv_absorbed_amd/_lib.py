@@ -97,6 +97,9 @@ def lib():
         L.mla_decode_partial_workspace_size.argtypes = [ctypes.POINTER(PartialArgs)]
         L.mla_decode_partial.restype = ci
         L.mla_decode_partial.argtypes = [ctypes.POINTER(PartialArgs), vp]
+        L.mla_decode_partial_pair.restype = ci
+        L.mla_decode_partial_pair.argtypes = [ctypes.POINTER(PartialArgs),
+                                              ctypes.POINTER(PartialArgs), vp]
         L.mla_q_absorb.restype = ci
         L.mla_q_absorb.argtypes = [vp, vp, vp, ci, ci, ci, vp]
         L.mla_vup.restype = ci
@@ -189,6 +192,11 @@ def mla_decode_partial_workspace_size(a: PartialArgs) -> int:
 
 def mla_decode_partial(a: PartialArgs, stream=None):
     _check(lib().mla_decode_partial(ctypes.byref(a), _stream(stream)), "mla_decode_partial")
+
+
+def mla_decode_partial_pair(hist: PartialArgs, cur: PartialArgs, stream=None):
+    _check(lib().mla_decode_partial_pair(ctypes.byref(hist), ctypes.byref(cur), _stream(stream)),
+           "mla_decode_partial_pair")
 
 
 def _host_i32(a):

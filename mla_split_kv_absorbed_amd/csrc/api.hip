@@ -106,23 +106,28 @@ int check_partial_args(const mla_partial_args* a) {
   return MLA_OK;
 }
 
-int check_partial_alias(const mla_partial_args* a, size_t ws) {
+// the call's input and output extents (the workspace counted as an output)
+void partial_extents(const mla_partial_args* a, size_t ws, Extent* ins, Extent* outs) {
   const size_t T = (size_t)a->B * a->S, H = a->H, P = a->P;
   const size_t e = elem_bytes(a->q_dtype);
   const size_t kv_rows = a->block_size > 0 ? (size_t)a->num_blocks * a->block_size
                                            : (size_t)a->B * a->kv_seq_stride;
-  Extent ins[7] = {{a->q_lat, T * H * kDc * e},
-                   {a->q_rope, T * H * kDr * e},
-                   {a->kv, kv_rows * kRow * e},
-                   {a->block_table, a->block_table ? (size_t)a->B * a->max_blocks * 4 : 0},
-                   {a->range_start, P * a->B * 4},
-                   {a->range_end, P * a->B * 4},
-                   {a->plan, a->plan ? (size_t)plan_table_words((long long)P * a->B, a->S,
-                                                                a->num_splits) * 4
-                                     : 0}};
-  Extent outs[3] = {{a->out, P * T * H * kDc * elem_bytes(a->out_dtype)},
-                    {a->lse, P * T * H * elem_bytes(a->lse_dtype)},
-                    {a->workspace, ws}};
+  ins[0] = {a->q_lat, T * H * kDc * e};
+  ins[1] = {a->q_rope, T * H * kDr * e};
+  ins[2] = {a->kv, kv_rows * kRow * e};
+  ins[3] = {a->block_table, a->block_table ? (size_t)a->B * a->max_blocks * 4 : 0};
+  ins[4] = {a->range_start, P * a->B * 4};
+  ins[5] = {a->range_end, P * a->B * 4};
+  ins[6] = {a->plan,
+            a->plan ? (size_t)plan_table_words((long long)P * a->B, a->S, a->num_splits) * 4 : 0};
+  outs[0] = {a->out, P * T * H * kDc * elem_bytes(a->out_dtype)};
+  outs[1] = {a->lse, P * T * H * elem_bytes(a->lse_dtype)};
+  outs[2] = {a->workspace, ws};
+}
+
+int check_partial_alias(const mla_partial_args* a, size_t ws) {
+  Extent ins[7], outs[3];
+  partial_extents(a, ws, ins, outs);
   if (any_overlap(outs, 3, ins, 7)) return MLA_ERR_ALIAS;
   if (any_misaligned({a->q_lat, a->q_rope, a->kv, a->out, ws ? a->workspace : nullptr}))
     return MLA_ERR_RANGE;
@@ -170,17 +175,8 @@ size_t partial_workspace_need(const mla_partial_args* a) {
 }
 
 // validation and launch of one partial call with the given workspace
-int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_bytes,
-                 void* stream) {
-  int st = check_partial_args(a);
-  if (st != MLA_OK) return st;
-  const size_t need = partial_ws_bytes(a);
-  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
-  mla_partial_args chk = *a;
-  chk.workspace = workspace;
-  st = check_partial_alias(&chk, need > 0 ? workspace_bytes : 0);
-  if (st != MLA_OK) return st;
-
+// kernel parameters of a validated call
+PartialParams partial_params(const mla_partial_args* a, void* workspace) {
   PartialParams pp;
   memset(&pp, 0, sizeof(pp));
   pp.q_lat = a->q_lat;
@@ -209,23 +205,74 @@ int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_by
   pp.scale = a->scale;
   pp.capacity = a->block_size > 0 ? (long long)a->max_blocks * a->block_size
                                   : (long long)a->kv_seq_stride;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (use_short(a)) {
-    e = launch_partial_short(pp, a->q_dtype, s);
-  } else if (use_mfma(a)) {
+  if (use_mfma(a)) {
     pp.ws_out = workspace;  // workspace base; the launcher lays it out
     pp.max_chunks = (int)mfma_max_chunks(a->B, a->S, a->P, a->num_splits);
-    e = launch_partial_mfma(pp, a->q_dtype, s);
-  } else {
-    e = launch_partial_simple(pp, a->q_dtype, s);
   }
+  return pp;
+}
+
+// argument, workspace and alias checks of one call
+int partial_check(const mla_partial_args* a, void* workspace, size_t workspace_bytes) {
+  int st = check_partial_args(a);
+  if (st != MLA_OK) return st;
+  const size_t need = partial_ws_bytes(a);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_ERR_WORKSPACE;
+  mla_partial_args chk = *a;
+  chk.workspace = workspace;
+  return check_partial_alias(&chk, need > 0 ? workspace_bytes : 0);
+}
+
+int partial_call(const mla_partial_args* a, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  const int st = partial_check(a, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  const PartialParams pp = partial_params(a, workspace);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (use_short(a))
+    e = launch_partial_short(pp, a->q_dtype, s);
+  else if (use_mfma(a))
+    e = launch_partial_mfma(pp, a->q_dtype, s);
+  else
+    e = launch_partial_simple(pp, a->q_dtype, s);
   return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // namespace mla
 
 extern "C" {
+
+int mla_decode_partial_pair(const mla_partial_args* hist, const mla_partial_args* cur,
+                            void* stream) {
+  if (!hist || !cur) return MLA_ERR_NULL;
+  int st = check_partial_args(hist);
+  if (st != MLA_OK) return st;
+  st = check_partial_args(cur);
+  if (st != MLA_OK) return st;
+  if (!use_mfma(hist) || !use_short(cur)) return MLA_ERR_UNSUPPORTED;
+  if (cur->q_dtype != hist->q_dtype) return MLA_ERR_DTYPE;
+  st = mla::partial_check(hist, hist->workspace, hist->workspace_bytes);
+  if (st != MLA_OK) return st;
+  st = mla::partial_check(cur, cur->workspace, cur->workspace_bytes);
+  if (st != MLA_OK) return st;
+  // neither call may write what the other reads or writes (the workgroups of
+  // both run at the same time)
+  const size_t hws = partial_ws_bytes(hist) > 0 ? hist->workspace_bytes : 0;
+  Extent ins[14], outs[6];
+  partial_extents(hist, hws, ins, outs);
+  partial_extents(cur, 0, ins + 7, outs + 3);
+  if (any_overlap(outs, 6, ins, 14)) return MLA_ERR_ALIAS;
+  const PartialParams hp = mla::partial_params(hist, hist->workspace);
+  const PartialParams cp = mla::partial_params(cur, nullptr);
+  // the combined grid's x extent: the history's bound plus the current call's
+  // workgroups
+  const long long hx = (long long)mla::mfma_max_chunks(hist->B, hist->S, hist->P,
+                                                      hist->num_splits) * hist->S + 8LL * hist->S;
+  if (hx + mla::pair_blocks(cp) > INT_MAX) return MLA_ERR_SHAPE;
+  const hipError_t e = mla::launch_partial_mfma(hp, hist->q_dtype, (hipStream_t)stream, &cp);
+  return e == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
 
 int mla_decode_partial_plan(const mla_partial_args* a, const int32_t* range_start,
                             const int32_t* range_end, mla_split_info* info) {

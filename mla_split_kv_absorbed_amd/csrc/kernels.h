@@ -48,7 +48,13 @@ constexpr int kShortKeys = 8;
 hipError_t launch_partial_short(const PartialParams& pp, int dtype, hipStream_t st);
 // MFMA path: q/kv dtype bf16 or f16, H % 128 == 0, block_size % 32 == 0 (or contiguous).
 bool mfma_path_supported(int dtype, int H, int block_size);
-hipError_t launch_partial_mfma(const PartialParams& pp, int dtype, hipStream_t st);
+// cur: a call of the short-range shape (bf16 / fp16 like pp, contiguous,
+// kv_seq_stride <= kShortKeys) run in the same grid behind the history's
+// chunks, or NULL
+hipError_t launch_partial_mfma(const PartialParams& pp, int dtype, hipStream_t st,
+                               const PartialParams* cur = nullptr);
+// workgroups a short-range call adds to a combined launch
+long long pair_blocks(const PartialParams& cur);
 // Upper bound on split sub-ranges ("slots") an MFMA-path call may write.
 size_t mfma_max_chunks(int B, int S, int P, int num_splits);
 size_t mfma_workspace_bytes(int B, int S, int H, int P, int num_splits, int out_dtype);

@@ -64,9 +64,11 @@
 // chunks come from an in-kernel plan, or, with an explicit split count, from
 // a closed form that needs no plan.
 #include "common.h"
+#include "short.h"
 #include "kernels.h"
 
 #include <algorithm>
+#include <cstring>
 #include <type_traits>
 
 namespace mla {
@@ -401,7 +403,18 @@ struct MfmaParams {
   PartialParams pp;
   int* ws_count;
   intx4* ws_desc;
+  // a combined launch (mla_decode_partial_pair): workgroups from cur_x0 on
+  // (head group 0 only) run the short-range call `cur`, kPairHeads heads per
+  // wave task; cur_x0 = 0 when there is none
+  PartialParams cur;
+  int cur_x0;
+  long long cur_tasks;
 };
+
+// heads per wave task of the current-chunk call in a combined launch: small
+// workgroups pack into the history's ragged end (4 and 8 measured alike, 16
+// and 1 slower)
+constexpr int kPairHeads = 4;
 
 // One LDS-direct load: 64 lanes x 16 bytes from the buffer `rs` at
 // voffset + soffset into LDS [m0, m0 + 1024) (lane i lands at m0 + 16 i).
@@ -416,8 +429,9 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t rs, unsigned m
                : "memory");
 }
 
-// kOneGroup: H == 128, one group of real heads (no head bound checks)
-template <typename T, bool kOneGroup>
+// kOneGroup: H == 128, one group of real heads (no head bound checks);
+// kPair: a combined launch with a current-chunk call (MfmaParams::cur)
+template <typename T, bool kOneGroup, bool kPair>
 __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const PartialParams& pp = mp.pp;
   typedef typename MT<T>::v8 v8;
@@ -437,6 +451,20 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int S = pp.S;
+
+  // A combined launch: the workgroups past the history chunks run the
+  // current-chunk call. They come last in dispatch order, so they fill the
+  // compute units that the history's longest-first schedule frees at its end.
+  if constexpr (kPair) {
+    if ((int)blockIdx.x >= mp.cur_x0) {
+      if (blockIdx.y == 0) {
+        const long long task = (long long)(blockIdx.x - mp.cur_x0) * 4 +
+                               __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+        if (task < mp.cur_tasks) short_task<T, kPairHeads>(mp.cur, task, threadIdx.x & 63);
+      }
+      return;
+    }
+  }
 
   // blockIdx -> (chunk, query): the S queries of one chunk sit 8 ids apart,
   // i.e. on the same XCD, so their shared key tiles meet in one L2
@@ -1211,8 +1239,14 @@ size_t mfma_workspace_bytes(int B, int S, int H, int P, int hint, int out_dtype)
   return ws_layout(B, S, H, P, hint, out_dtype).total;
 }
 
-hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_t st) {
+long long pair_blocks(const PartialParams& cur) {
+  return (short_tasks(cur, kPairHeads) + 3) / 4;
+}
+
+hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_t st,
+                               const PartialParams* cur) {
   MfmaParams mp;
+  memset(&mp, 0, sizeof(mp));
   mp.pp = pp_in;
   const WsLayout w = ws_layout(pp_in.B, pp_in.S, pp_in.H, pp_in.P, pp_in.num_splits, pp_in.out_dtype);
   char* ws = (char*)pp_in.ws_out;  // base of the workspace
@@ -1231,19 +1265,32 @@ hipError_t launch_partial_mfma(const PartialParams& pp_in, int dtype, hipStream_
                                    : mfma_max_chunks(pp_in.B, pp_in.S, pp_in.P, pp_in.num_splits);
   size_t groups = chunks * pp_in.S;
   if (pp_in.S > 1) groups = (groups + 8 * pp_in.S - 1) / (8 * pp_in.S) * (8 * pp_in.S);
-  // blockIdx.y: the group of 128 heads
-  dim3 grid((unsigned)groups, (unsigned)((pp_in.H + kHeadsGroup - 1) / kHeadsGroup));
+  // blockIdx.y: the group of 128 heads; a current-chunk call rides behind
+  // the history's chunks in x
+  long long gx = (long long)groups;
+  if (cur) {
+    mp.cur = *cur;
+    mp.cur_x0 = (int)groups;
+    mp.cur_tasks = short_tasks(*cur, kPairHeads);
+    gx += pair_blocks(*cur);
+  }
+  dim3 grid((unsigned)gx, (unsigned)((pp_in.H + kHeadsGroup - 1) / kHeadsGroup));
   const bool one = pp_in.H == kHeadsGroup;
+  auto launch = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, mp); };
   if (dtype == MLA_BF16) {
-    if (one)
-      hipLaunchKernelGGL((partial_mfma_kernel<bf16, true>), grid, dim3(256), 0, st, mp);
+    if (cur)
+      one ? launch(partial_mfma_kernel<bf16, true, true>)
+          : launch(partial_mfma_kernel<bf16, false, true>);
     else
-      hipLaunchKernelGGL((partial_mfma_kernel<bf16, false>), grid, dim3(256), 0, st, mp);
+      one ? launch(partial_mfma_kernel<bf16, true, false>)
+          : launch(partial_mfma_kernel<bf16, false, false>);
   } else {
-    if (one)
-      hipLaunchKernelGGL((partial_mfma_kernel<f16, true>), grid, dim3(256), 0, st, mp);
+    if (cur)
+      one ? launch(partial_mfma_kernel<f16, true, true>)
+          : launch(partial_mfma_kernel<f16, false, true>);
     else
-      hipLaunchKernelGGL((partial_mfma_kernel<f16, false>), grid, dim3(256), 0, st, mp);
+      one ? launch(partial_mfma_kernel<f16, true, false>)
+          : launch(partial_mfma_kernel<f16, false, false>);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

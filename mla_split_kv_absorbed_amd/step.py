@@ -33,7 +33,7 @@ class DecodeStep:
                  num_splits: int = 0, flags: int = 0, q_lat_in: Optional[np.ndarray] = None,
                  side_stream: bool = False, fused_tail: bool = True, keep_latent: bool = False,
                  host_subranges: bool = False, auto_plan: bool = False,
-                 host_plan: bool = False):
+                 host_plan: bool = False, pair_current: bool = False):
         """num_splits: 0 lets the library plan; for equal ranges the plan's
         chunk count is then passed explicitly (the kernel skips its plan)
         unless auto_plan is set.
@@ -41,6 +41,10 @@ class DecodeStep:
         ranges, or auto_plan), the plan is built on the host from the ranges
         (mla_decode_partial_make_plan) and handed to the call in device
         memory, as a serving loop that holds its sequence lengths would.
+        pair_current: when the current-chunk call takes the short-range
+        kernel and the history call the matrix-core kernel, both run as one
+        launch (mla_decode_partial_pair) instead of two; not with
+        side_stream.
         host_subranges: a single part without a current chunk, whose
         ranges the partial call would cut into k > 1 sub-ranges (equal ranges,
         bf16 / fp16), is instead cut on the host (cut_ranges) and passed as k
@@ -134,6 +138,12 @@ class DecodeStep:
         # workspace: a workspace belongs to one call until its stream has
         # passed it. Every buffer it touches is owned by this object for its
         # whole life, so no allocator stream bookkeeping is needed.
+        self.pair = False
+        if pair_current and sp.current and not side_stream:
+            hist_path = L.mla_decode_partial_plan(self.hist_args, rs, re_).matrix_path
+            cur_path = L.mla_decode_partial_plan(self.cur_args, np.zeros(B, np.int32),
+                                                 np.full(B, S, np.int32)).matrix_path
+            self.pair = hist_path == 1 and cur_path == 2
         self.side = None
         if side_stream and sp.current:
             self.side = torch.cuda.Stream(device=dev)  # default priority
@@ -187,6 +197,10 @@ class DecodeStep:
             self.ev_cur.record(self.side)
             L.mla_decode_partial(self.hist_args, main)
             main.wait_event(self.ev_cur)
+        elif self.pair:
+            L.mla_decode_partial_pair(self.hist_args, self.cur_args, main)
+            if "current_done" in marks:
+                marks["current_done"].record(main)
         else:
             L.mla_decode_partial(self.hist_args, main)
             if self.w.spec.current:

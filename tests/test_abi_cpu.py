@@ -256,3 +256,45 @@ def test_contiguous_short_range_routing(dtype, stride, flags, path):
     if path != 1:
         a.plan, a.plan_chunks = FAKE + 0x48000000, 1
         assert call(a) == -6  # MLA_ERR_UNSUPPORTED
+
+
+def pair_args(**cur_over):
+    """A history call on the matrix kernel and a current-chunk call (2 keys
+    per sequence, contiguous) reading the same queries."""
+    hist = base_args()
+    cur = base_args(block_size=0, block_table=None, kv_seq_stride=2, kv=FAKE + 0x28000000,
+                    range_start=FAKE + 0x40002000, range_end=FAKE + 0x40003000, P=1,
+                    out=FAKE + 0x58000000, lse=FAKE + 0x68000000, workspace=None,
+                    workspace_bytes=0, mask=L.MLA_MASK_CAUSAL_WINDOW)
+    for k, v in cur_over.items():
+        setattr(cur, k, v)
+    return hist, cur
+
+
+def call_pair(hist, cur):
+    return L.lib().mla_decode_partial_pair(ctypes.byref(hist), ctypes.byref(cur), None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(kv_seq_stride=9), -6),                       # current call not short-range
+    (dict(flags=L.MLA_FLAG_FORCE_SIMPLE), -6),
+    (dict(q_dtype=L.MLA_F16, kv_dtype=L.MLA_F16), -3),  # dtypes differ
+    (dict(out=FAKE + 0x10000000), -8),                 # current output over the shared q_rope
+    (dict(out=FAKE + 0x50000000 + 256), -8),           # current output over the history output
+    (dict(lse=FAKE + 0x70000000 + 64), -8),            # current LSE inside the history workspace
+    (dict(kv=None), -1),
+])
+def test_pair_validation(over, code):
+    """Both calls are validated as single calls, then as a pair: the history
+    on the matrix kernel, the current call on the short-range kernel, one
+    dtype, and no output of either over anything the other touches (the
+    shared queries are allowed). Nothing is launched on error."""
+    hist, cur = pair_args(**over)
+    assert call_pair(hist, cur) == code
+
+
+def test_pair_valid_call_without_device_reports_hip_error():
+    hist, cur = pair_args()
+    assert call_pair(hist, cur) == -7
+    hist.flags = L.MLA_FLAG_FORCE_SIMPLE
+    assert call_pair(hist, cur) == -6
