@@ -275,8 +275,10 @@ int mla_decode_partial(const mla_partial_args* a, void* stream);
  * come after the history's chunks in dispatch order, so they run on the
  * compute units the history's schedule frees at its end. Neither call's
  * outputs (or hist's workspace) may overlap anything the other reads or
- * writes (MLA_ERR_ALIAS); reading the same queries is allowed. Outputs are
- * bitwise those of the two separate calls. */
+ * writes (MLA_ERR_ALIAS); reading the same queries is allowed. A pair whose
+ * combined grid would pass 2^31 - 1 workgroups is MLA_ERR_SHAPE (the two
+ * calls can then be made separately). Outputs are bitwise those of the two
+ * separate calls. */
 int mla_decode_partial_pair(const mla_partial_args* hist, const mla_partial_args* cur,
                             void* stream);
 
