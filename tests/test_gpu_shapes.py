@@ -119,3 +119,28 @@ def test_partial_causal_window_long(S, dtype, splits):
             fin = ~empty
             assert (np.abs(g_o - o) - half_ulp(o, sp.part_out_dtype))[fin].max() <= otol
             assert np.all(np.abs(g_l - l)[fin] <= ltol + half_ulp(l[fin], sp.part_lse_dtype))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_partial_long_sequence(dtype):
+    """One sequence of 256K keys, the longest here: the plan cuts its range
+    into 256 pieces (the workspace's largest use at one range), merged inside
+    the call; sampled heads of the merged part against the oracle."""
+    wid = 2 if dtype == "bf16" else 4
+    sp = W.spec(wid, B=1, lengths=("fixed", 262144), parts=1)
+    say(f"[long] {dtype} L=262144")
+    w = W.make_workload(sp)
+    qs = oracle_qlat(w)
+    st = DecodeStep(w, q_lat_in=qs)
+    assert st.num_splits > 1
+    L.mla_decode_partial(st.hist_args)
+    torch.cuda.synchronize()
+    heads = [0, 45, 127]
+    ql, qr = W.from_storage(qs, sp.dtype), w.f64("q_rope")
+    o, l = mo.latent_partial(ql[:, heads], qr[:, heads], w.seq_rows64(0),
+                             int(w.range_start[0, 0]), int(w.range_end[0, 0]), sp.scale)
+    go, gl = f64(st.parts_out)[0][:, heads], f64(st.parts_lse)[0][:, heads]
+    otol, ltol = TOL[sp.dtype]
+    assert np.all(np.isfinite(go)) and np.all(np.isfinite(gl))
+    assert (np.abs(go - o) - half_ulp(o, sp.part_out_dtype)).max() <= otol
+    assert np.all(np.abs(gl - l) <= ltol + half_ulp(l, sp.part_lse_dtype))

@@ -3,7 +3,7 @@ partial call, each against the float64 oracle: batch sizes, head counts,
 query lengths, block sizes (paged 32 / 64 / 128 and contiguous), part
 counts, explicit and automatic split counts, ragged and empty ranges, and
 the three storage types; every other case with the split plan built on the
-host. Sizes stay small enough for the oracle to finish in seconds per case."""
+host, and half the cases with a current chunk in the history call's launch. Sizes stay small enough for the oracle to finish in seconds per case."""
 import numpy as np
 import pytest
 import torch
@@ -46,8 +46,10 @@ def test_sweep_step_and_partial(i):
     say(f"[sweep {i}] {over} splits={splits}")
     w = W.make_workload(sp)
     # the whole step (absorb, partial over the parts [+ current], combine, V-up);
-    # every other case hands the partial call a plan built on the host
-    st = DecodeStep(w, num_splits=splits, auto_plan=splits == 0, host_plan=i % 2 == 0)
+    # every other case hands the partial call a plan built on the host, and
+    # every other case with a current chunk runs it in the history's launch
+    st = DecodeStep(w, num_splits=splits, auto_plan=splits == 0, host_plan=i % 2 == 0,
+                    pair_current=i % 4 < 2)
     st.run()
     torch.cuda.synchronize()
     extra = sp.part_lse_dtype if sp.part_lse_dtype != "f32" else None
