@@ -481,6 +481,35 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     sh_found.u = -1;
     sh_redo = 0;
   }
+  // ---- Q^T for this wave's 32 heads, in registers -------------------------
+  // requested as soon as the range index is known, ahead of the range's own
+  // round trip (lane quantities read afresh here: the per-lane constants
+  // below keep their own definitions for the tile loop's address arithmetic)
+  v8 q[kKSteps];
+  auto load_q = [&](int u) __attribute__((always_inline)) {
+    const int ql_lane = threadIdx.x & 63;
+    const int qhi = ql_lane >> 5;
+    const int qhead =
+        __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) * kHeadsWave + (ql_lane & 31);
+    const int qhead0 = kOneGroup ? 0 : blockIdx.y * kHeadsGroup;
+    const bool qok = kOneGroup || qhead0 + qhead < pp.H;
+    // a missing head (beyond H) loads a real row and zeroes it: every lane
+    // issues the same loads
+    const int tq = (u % pp.B) * S + s;
+    const int hq = qok ? qhead0 + qhead : pp.H - 1;
+    const T* ql = (const T*)pp.q_lat + ((size_t)tq * pp.H + hq) * kDc;
+    const T* qr = (const T*)pp.q_rope + ((size_t)tq * pp.H + hq) * kDr;
+#pragma unroll
+    for (int k = 0; k < kKSteps; ++k) {
+      const int d = k * 16 + qhi * 8;
+      q[k] = d < kDc ? *(const v8*)(ql + d) : *(const v8*)(qr + (d - kDc));
+    }
+    if (!qok)
+#pragma unroll
+      for (int k = 0; k < kKSteps; ++k)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) q[k][i] = (T)0.f;
+  };
   Found fd;
   bool first;  // this piece is the first of its range
   if (pp.plan) {
@@ -492,6 +521,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     const int* e = pp.plan + kPlanHeader + (size_t)chunk * kPlanEntry;
     const int u = __builtin_amdgcn_readfirstlane(e[0]);
     if (u < 0 || u >= pp.P * pp.B) return;
+    load_q(u);
     const Unit x = load_unit(pp, u);
     const int tb = min(max(__builtin_amdgcn_readfirstlane(e[1]), 0), x.nt);
     const int te = min(max(__builtin_amdgcn_readfirstlane(e[2]), tb), x.nt);
@@ -531,6 +561,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
       u = chunk / k;
       i = chunk % k;
     }
+    load_q(u);
     const Unit x = load_unit(pp, u);
     fd.u = u;
     fd.tb = piece_tile(i, x.nt, k);
@@ -552,6 +583,7 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *mp.ws_count = pl.nsplit_units;
     fd.u = __builtin_amdgcn_readfirstlane(sh_found.u);
     if (fd.u < 0) return;  // grid slack beyond the plan's chunks
+    load_q(fd.u);
     fd.tb = __builtin_amdgcn_readfirstlane(sh_found.tb);
     fd.te = __builtin_amdgcn_readfirstlane(sh_found.te);
     fd.slot = __builtin_amdgcn_readfirstlane(sh_found.slot);
@@ -621,25 +653,6 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
   const unsigned lds_base =
       __builtin_amdgcn_readfirstlane((unsigned)(size_t)(LDS_AS char*)lds);
 
-  // ---- Q^T for this wave's 32 heads, in registers -------------------------
-  v8 q[kKSteps];
-  {
-    // a missing head (beyond H) loads a real row and zeroes it: every lane
-    // issues the same loads
-    const int hq = head_ok ? head0 + head : pp.H - 1;
-    const T* ql = (const T*)pp.q_lat + ((size_t)t * pp.H + hq) * kDc;
-    const T* qr = (const T*)pp.q_rope + ((size_t)t * pp.H + hq) * kDr;
-#pragma unroll
-    for (int k = 0; k < kKSteps; ++k) {
-      const int d = k * 16 + hi * 8;
-      q[k] = d < kDc ? *(const v8*)(ql + d) : *(const v8*)(qr + (d - kDc));
-    }
-    if (!head_ok)
-#pragma unroll
-      for (int k = 0; k < kKSteps; ++k)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) q[k][i] = (T)0.f;
-  }
   // The Q loads complete at the row table's wait (fill_rows), before the
   // first tile load: with nothing pending at loop entry the compiler places
   // no vmcnt waits of its own inside the tile loop (it cannot see the
