@@ -937,11 +937,11 @@ __global__ __launch_bounds__(256, 1) void partial_mfma_kernel(MfmaParams mp) {
     const int nvis = min(vend, min(en, (st_tile + j + 1) * kTile)) - tok0;
     if (nvis < kTile) {
       qk_drain(sacc);
+      // row 8 (i >> 2) + 4 hi + (i & 3) is visible when below nvis: the
+      // per-i part is a constant, so no row index stays live in the loop
+      const int lim = nvis - 4 * hi;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 8 * (i >> 2) + 4 * hi + (i & 3);
-        sacc[i] = row < nvis ? sacc[i] : -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i) sacc[i] = 8 * (i >> 2) + (i & 3) < lim ? sacc[i] : -INFINITY;
     }
     __builtin_amdgcn_sched_barrier(0);
 
