@@ -14,9 +14,10 @@ import numpy as np
 import pytest
 import torch
 
+from mla_split_kv_absorbed_amd import _lib as L
 from mla_split_kv_absorbed_amd import workloads as W
 from mla_split_kv_absorbed_amd.step import DecodeStep
-from tests.test_gpu_parity import check_step, say
+from tests.test_gpu_parity import check_step, oracle_qlat, say
 
 pytestmark = pytest.mark.gpu
 
@@ -56,3 +57,35 @@ def test_pair_step(case):
     heads = list(range(0, sp.H, 9))
     extra = sp.part_lse_dtype if sp.part_lse_dtype != "f32" else None
     check_step(w, pair, seqs, heads, extra)
+
+
+def test_pair_invalid_ranges_are_contained():
+    """Invalid ranges in either call of a pair (a history range starting
+    below 0, a current range ending past the chunk) give NaN rows for those
+    ranges only, exactly as the two separate calls do."""
+    sp = W.spec(3, B=4, lengths=("uniform", 100, 900))
+    say("[pair] invalid ranges")
+    w = W.make_workload(sp)
+    qs = oracle_qlat(w)  # the partial calls alone read q_lat: set it
+    ser = DecodeStep(w, q_lat_in=qs)
+    pair = DecodeStep(w, q_lat_in=qs, pair_current=True)
+    assert pair.pair
+    for st in (ser, pair):
+        st.range_start[1, 2] = -1
+        st.cur_end[0, 3] = sp.S + 1
+        st.parts_out.fill_(0.5)
+        st.cur_out.fill_(0.5)
+        if st is ser:
+            L.mla_decode_partial(st.hist_args)
+            L.mla_decode_partial(st.cur_args)
+        else:
+            L.mla_decode_partial_pair(st.hist_args, st.cur_args)
+    torch.cuda.synchronize()
+    assert torch.equal(pair.parts_out.isnan(), ser.parts_out.isnan())
+    assert torch.equal(pair.parts_out.nan_to_num(7.0), ser.parts_out.nan_to_num(7.0))
+    assert torch.equal(pair.cur_out.nan_to_num(7.0), ser.cur_out.nan_to_num(7.0))
+    assert torch.equal(pair.cur_lse.nan_to_num(7.0), ser.cur_lse.nan_to_num(7.0))
+    S = sp.S
+    assert bool(pair.parts_out[1, 2 * S:3 * S].isnan().all())
+    assert bool(pair.cur_out[3 * S:4 * S].isnan().all())
+    assert not bool(pair.cur_out[:3 * S].isnan().any())
