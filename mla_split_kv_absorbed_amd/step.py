@@ -1,7 +1,8 @@
-"""One absorbed split-KV MLA decode step on the device, as four library calls:
+"""One absorbed split-KV MLA decode step on the device, as library calls:
 
-  mla_q_absorb -> mla_decode_partial (history parts [+ current chunk])
-  -> mla_lse_combine -> mla_vup
+  mla_q_absorb -> mla_decode_partial (history parts [+ current chunk], or
+  both in one launch: mla_decode_partial_pair) -> mla_lse_combine -> mla_vup
+  (the last two as one launch: mla_combine_vup)
 
 This module only uploads a workload, allocates the outputs and marshals
 arguments; all arithmetic happens in libmla_decode.so.
@@ -133,17 +134,19 @@ class DecodeStep:
             self.hist_args.plan = self.plan.data_ptr()
             self.hist_args.plan_chunks = info.chunks
             self.hist_args.plan_split_units = info.split_ranges
-        # Current-chunk attention on a side stream, concurrent with the
-        # history partial (the study page's stream split). It gets its own
-        # workspace: a workspace belongs to one call until its stream has
-        # passed it. Every buffer it touches is owned by this object for its
-        # whole life, so no allocator stream bookkeeping is needed.
+        # the history and the current-chunk calls in one launch, when their
+        # kernels allow it
         self.pair = False
         if pair_current and sp.current and not side_stream:
             hist_path = L.mla_decode_partial_plan(self.hist_args, rs, re_).matrix_path
             cur_path = L.mla_decode_partial_plan(self.cur_args, np.zeros(B, np.int32),
                                                  np.full(B, S, np.int32)).matrix_path
             self.pair = hist_path == 1 and cur_path == 2
+        # Current-chunk attention on a side stream, concurrent with the
+        # history partial (the study page's stream split). It gets its own
+        # workspace: a workspace belongs to one call until its stream has
+        # passed it. Every buffer it touches is owned by this object for its
+        # whole life, so no allocator stream bookkeeping is needed.
         self.side = None
         if side_stream and sp.current:
             self.side = torch.cuda.Stream(device=dev)  # default priority
