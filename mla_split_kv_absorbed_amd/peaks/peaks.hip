@@ -9,7 +9,9 @@
 //     isolation: a dependent 32x32x16 chain accumulating in VGPRs, one
 //     16-byte key read per instruction fetched 8 instructions ahead, a 1 KB
 //     LDS-direct load every 4 instructions and a workgroup barrier every 36,
-//     four waves per compute unit.
+//     four waves per compute unit;
+//   - the whole tile loop's pattern (score product, weights, value product,
+//     tiles streamed from HBM) at one and at two waves per SIMD.
 // One JSON object is printed on stdout. Every kernel is launched on all
 // compute units; LDS and HBM addresses stay inside their buffers.
 #include <hip/hip_runtime.h>
@@ -220,6 +222,173 @@ __global__ __launch_bounds__(256, 1) void lds_stream_kernel(unsigned long long* 
   if (tid == 0) cyc[blockIdx.x] = t1 - t0;
 }
 
+// ---- the tile loop at one and at two waves per SIMD ----------------------------
+// Two ways to split the partial kernel's tile loop over the waves of a compute
+// unit, with the same matrix work per SIMD (2176 cycles per 32-key tile of 128
+// heads) and the same cache stream (36 KB tiles through LDS-direct loads into
+// a 4-stage ring, the loads of tile j + 2 issued in step j):
+//   W = 4 (one wave per SIMD): 32 heads per wave; score product 36 dependent
+//     32x32x16 products; value product 128 heads x 128 latent columns per
+//     wave, 32 products into 16 accumulator tiles;
+//   W = 8 (two waves per SIMD): 16 heads per wave; score product 2 x 18
+//     dependent 16x16x32 products; value product 128 heads x 64 columns per
+//     wave, 16 products into 8 accumulator tiles.
+// Step j: wait for tile j's loads, barrier, issue tile j + 2; the score
+// product of tile j, every wave reading the whole key tile (one 16-byte read
+// per product); the value product of tile j - 1, reading all 128 heads'
+// weights (8 KB) and the wave's columns of that tile's values (transposed
+// 8-byte reads); tile j's weights from the scores (scale, exp2, sum, convert
+// to bf16) into the other of two weight buffers. LDS reads per tile and CU:
+// keys 144 KB, weights 32 KB, values 32 KB at W = 4; keys 288 KB, weights
+// 64 KB, values 32 KB at W = 8. The query operand is one register (which
+// register a product reads does not change its cost). Softmax bookkeeping
+// beyond that minimum, masking, the chunk's start and its output epilogue are
+// left out: the figures bound what each design's loop can reach.
+constexpr int kPatTiles = 192;  // tiles per workgroup and launch; every block read once
+constexpr int kPatStage = 36864;
+constexpr int kPatRow = 1152;  // bytes per key row in a tile (576 bf16)
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+template <int W>
+__global__ __launch_bounds__(W * 64, 1) void pattern_kernel(float* out, unsigned long long* cyc,
+                                                            const char* src, int src_blocks) {
+  static_assert(W == 4 || W == 8, "one or two waves per SIMD");
+  // 4 stages of 36 KB, then 2 weight buffers of 128 heads x 32 keys (bf16)
+  __shared__ __attribute__((aligned(1024))) char lds[4 * kPatStage + 2 * 8192];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, src_blocks * 1024, 0x00020000);
+  const unsigned ldsb = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(LDS_AS char*)lds);
+  // the 36 loads of 1 KB per tile: 9 per wave, or 5 for waves 0-3 and 4 for 4-7
+  const int nl = W == 4 ? 9 : (wave < 4 ? 5 : 4);
+  const int lb = W == 4 ? wave * 9 : (wave < 4 ? wave * 5 : 20 + (wave - 4) * 4);
+  const int first = blockIdx.x * kPatTiles * 36;
+  auto issue = [&](int j) {
+    const int t = j < kPatTiles ? j : j - kPatTiles;  // the last two re-read the first tiles
+    for (int i = 0; i < nl; ++i)
+      lds_load16(rs, ldsb + (j & 3) * kPatStage + (lb + i) * 1024, lane * 16,
+                 (first + t * 36 + lb + i) * 1024);
+  };
+  auto wait_tile = [&] {  // at most the next tile's loads outstanding
+    if constexpr (W == 4) {
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    } else {
+      if (wave < 4)
+        asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    }
+  };
+  bf16x8 q;
+  for (int i = 0; i < 8; ++i) q[i] = (__bf16)(0.001f * (lane & 7));
+  constexpr int NB = W == 4 ? 4 : 2;   // 32-column blocks of the value product per wave
+  constexpr int NE = W == 4 ? 16 : 8;  // scores per lane and tile
+  floatx16 o[4][NB];
+  for (int m = 0; m < 4; ++m)
+    for (int n = 0; n < NB; ++n) o[m][n] = floatx16{};
+  float lsum = 0.f;
+  const unsigned long long t0 = clk();
+  issue(0);
+  issue(1);
+  for (int j = 0; j < kPatTiles; ++j) {
+    wait_tile();
+    __syncthreads();  // tile j and tile j - 1's weights visible; step j - 1 done everywhere
+    issue(j + 2);     // into the stage that tile j - 2 held
+    const char* tile = lds + (j & 3) * kPatStage;
+    // key operands read 8 products ahead through a ring of 8 registers; the
+    // order of reads and products is fixed (no hoisting of all 36 reads)
+    float e[NE];
+    bf16x8 kr[8];
+    auto key = [&](int n) { return *(const LDS_AS bf16x8*)(tile + n * 1024 + lane * 16); };
+#pragma unroll
+    for (int n = 0; n < 8; ++n) kr[n] = key(W == 4 ? n : (n & 1) * 18 + (n >> 1));
+    if constexpr (W == 4) {
+      // the scores in VGPRs (the 256 accumulator registers hold the output)
+      floatx16 s;
+#pragma unroll
+      for (int n = 0; n < 36; ++n) {
+        if (n == 0)  // the chain starts from zero
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(s) : "v"(q), "v"(kr[0]));
+        else
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                       : "+v"(s)
+                       : "v"(q), "v"(kr[n & 7]));
+        if (n + 8 < 36) kr[n & 7] = key(n + 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s));  // chain result ready
+      for (int i = 0; i < 16; ++i) e[i] = s[i];
+    } else {
+      // products alternate between the two 16-key blocks: product n reads
+      // block n & 1 at depth n >> 1
+      floatx4 s0 = {}, s1 = {};
+#pragma unroll
+      for (int n = 0; n < 36; ++n) {
+        if (n & 1)
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, kr[n & 7], s1, 0, 0, 0);
+        else
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(q, kr[n & 7], s0, 0, 0, 0);
+        if (n + 8 < 36) kr[n & 7] = key(((n + 8) & 1) * 18 + ((n + 8) >> 1));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int i = 0; i < 4; ++i) {
+        e[i] = s0[i];
+        e[4 + i] = s1[i];
+      }
+    }
+    {  // value product of tile j - 1 with its weights (at j = 0: stale LDS, timing only)
+      const char* pt = lds + ((j - 1) & 3) * kPatStage;
+      const char* pw = lds + 4 * kPatStage + ((j - 1) & 1) * 8192;
+      const int col0 = wave * (NB * 32);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 v[NB];
+#pragma unroll
+        for (int n = 0; n < NB; ++n) {
+          const char* p = pt + (kb * 16 + (lane & 15)) * kPatRow +
+                          (col0 + n * 32 + (lane >> 4) * 8) * 2;
+          const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)p);
+          const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS shortx4*)(p + 8));
+          for (int i = 0; i < 4; ++i) {
+            v[n][i] = __builtin_bit_cast(__bf16, lo[i]);
+            v[n][4 + i] = __builtin_bit_cast(__bf16, hi[i]);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const bf16x8 a = *(const LDS_AS bf16x8*)(pw + (m * 2 + kb) * 1024 + lane * 16);
+#pragma unroll
+          for (int n = 0; n < NB; ++n)
+            o[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, v[n], o[m][n], 0, 0, 0);
+        }
+      }
+    }
+    // tile j's weights: 2 KB (W = 4) or 1 KB (W = 8) per wave
+    bf16x8 wv[NE / 8];
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const float x = __builtin_amdgcn_exp2f(fmaf(e[i], 0.0625f, -1.f));
+      lsum += x;
+      wv[i / 8][i % 8] = (__bf16)x;
+    }
+    char* pw = lds + 4 * kPatStage + (j & 1) * 8192;
+#pragma unroll
+    for (int i = 0; i < NE / 8; ++i)
+      *(LDS_AS bf16x8*)(pw + wave * (NE * 128) + i * 1024 + lane * 16) = wv[i];
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  const unsigned long long t1 = clk();
+  // the accumulators stay live (and in accumulator registers) to the end
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) asm volatile("" ::"a"(o[m][n]));
+  out[blockIdx.x * (W * 64) + tid] = lsum;
+  if (lane == 0) cyc[blockIdx.x * W + wave] = t1 - t0;
+}
+
 // ---- host ------------------------------------------------------------------
 template <typename F>
 static float best_ms(F launch, int reps) {
@@ -323,6 +492,28 @@ int main() {
   stream(lds_stream_kernel<4>, 4);
   const double chain_cyc = mean_cycles(ccyc, cus * 4) / (kChainIters * 36.0);
   CHECK(hipGetLastError());
+
+  // the tile loop at one and at two waves per SIMD
+  if ((size_t)cus * kPatTiles * 36 > (size_t)src_blocks) {
+    fprintf(stderr, "tile-loop source too small\n");
+    return 1;
+  }
+  unsigned long long* pcyc;
+  CHECK(hipMalloc(&pcyc, (size_t)cus * 8 * sizeof(unsigned long long)));
+  double pat_gbs[2], pat_cyc[2], pat_ghz[2];
+  auto pattern = [&](auto kernel, int waves, int k) {
+    const float ms = best_ms([&] {
+      hipLaunchKernelGGL(kernel, dim3(cus), dim3(waves * 64), 0, 0, sink, pcyc,
+                         (const char*)src, src_blocks);
+    }, 5);
+    const double c = mean_cycles(pcyc, cus * waves);
+    pat_gbs[k] = (double)cus * (kPatTiles + 2) * 36 * 1024 / (ms * 1e-3) / 1e9;
+    pat_cyc[k] = c / kPatTiles;
+    pat_ghz[k] = c / (ms * 1e6);
+  };
+  pattern(pattern_kernel<4>, 4, 0);
+  pattern(pattern_kernel<8>, 8, 1);
+  CHECK(hipGetLastError());
   CHECK(hipDeviceSynchronize());
 
   const double lds_bytes_cu = 4.0 * kLdsIters * 8 * 1024;  // per CU per launch
@@ -335,7 +526,13 @@ int main() {
          "\"lds_b128_tbs\": %.1f, \"lds_tr_b64_tbs\": %.1f, "
          "\"score_chain_cycles_per_mfma\": %.2f, \"score_chain_hbm_gbs\": %.1f, "
          "\"score_chain_clock_ghz\": %.3f, \"hbm_read_lds_direct_gbs\": %.1f, "
-         "\"hbm_read_lds_direct_gbs_by_tiles_in_flight\": [%.1f, %.1f, %.1f, %.1f]}\n",
+         "\"hbm_read_lds_direct_gbs_by_tiles_in_flight\": [%.1f, %.1f, %.1f, %.1f], "
+         "\"tile_loop_1_wave_per_simd_hbm_gbs\": %.1f, "
+         "\"tile_loop_1_wave_per_simd_cycles_per_tile\": %.0f, "
+         "\"tile_loop_1_wave_per_simd_clock_ghz\": %.3f, "
+         "\"tile_loop_2_waves_per_simd_hbm_gbs\": %.1f, "
+         "\"tile_loop_2_waves_per_simd_cycles_per_tile\": %.0f, "
+         "\"tile_loop_2_waves_per_simd_clock_ghz\": %.3f}\n",
          prop.gcnArchName, cus, rbytes / (ms_read * 1e-3) / 1e9,
          2.0 * cbytes / (ms_copy * 1e-3) / 1e9, mfma_flop / (ms_mfma * 1e-3) / 1e12,
          mfma_cyc / (kMfmaIters * 4.0), mfma_cyc / (ms_mfma * 1e6),
@@ -343,11 +540,13 @@ int main() {
          lds_bytes_cu * cus / (ms_lds * 1e-3) / 1e12, tr_bytes_cu * cus / (ms_tr * 1e-3) / 1e12,
          chain_cyc, chain_bytes / (ms_chain * 1e-3) / 1e9,
          chain_cyc * kChainIters * 36.0 / (ms_chain * 1e6),
-         stream_gbs[2], stream_gbs[1], stream_gbs[2], stream_gbs[3], stream_gbs[4]);
+         stream_gbs[2], stream_gbs[1], stream_gbs[2], stream_gbs[3], stream_gbs[4],
+         pat_gbs[0], pat_cyc[0], pat_ghz[0], pat_gbs[1], pat_cyc[1], pat_ghz[1]);
   CHECK(hipFree(src));
   CHECK(hipFree(dst));
   CHECK(hipFree(sink));
   CHECK(hipFree(cyc));
   CHECK(hipFree(ccyc));
+  CHECK(hipFree(pcyc));
   return 0;
 }
