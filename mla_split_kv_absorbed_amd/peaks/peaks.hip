@@ -281,8 +281,8 @@ __global__ __launch_bounds__(W * 64, 1) void pattern_kernel(float* out, unsigned
         asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     }
   };
-  bf16x8 q;
-  for (int i = 0; i < 8; ++i) q[i] = (__bf16)(0.001f * (lane & 7));
+  bf16x8 q;  // query values of the size the keys have, varied over lanes and elements
+  for (int i = 0; i < 8; ++i) q[i] = (__bf16)(0.0625f * (float)((lane * 8 + i) % 15 - 7));
   constexpr int NB = W == 4 ? 4 : 2;   // 32-column blocks of the value product per wave
   constexpr int NE = W == 4 ? 16 : 8;  // scores per lane and tile
   floatx16 o[4][NB];
@@ -389,6 +389,23 @@ __global__ __launch_bounds__(W * 64, 1) void pattern_kernel(float* out, unsigned
   if (lane == 0) cyc[blockIdx.x * W + wave] = t1 - t0;
 }
 
+// Source data for the loops that multiply what they load: bf16 pairs spread
+// over (-1, 1) from a hash of the word index (matrix-core power, and with it
+// the clock under a power limit, depends on the operands; zeros would flatter it).
+__global__ __launch_bounds__(256) void fill_kernel(unsigned* __restrict__ p, size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    unsigned h = (unsigned)i * 0x9E3779B1u;
+    h ^= h >> 15;
+    h *= 0x85EBCA77u;
+    h ^= h >> 13;
+    // each half: sign, exponent 119..126 (magnitudes 2^-8 .. 1), 7 random mantissa bits
+    const unsigned lo = (h & 0x8000u) | ((119u + ((h >> 7) & 7u)) << 7) | (h & 0x7Fu);
+    const unsigned hi = ((h >> 16) & 0x8000u) | ((119u + ((h >> 23) & 7u)) << 7) | ((h >> 16) & 0x7Fu);
+    p[i] = lo | (hi << 16);
+  }
+}
+
 // ---- host ------------------------------------------------------------------
 template <typename F>
 static float best_ms(F launch, int reps) {
@@ -431,7 +448,9 @@ int main() {
   float* sink;
   CHECK(hipMalloc(&src, rbytes));
   CHECK(hipMalloc(&dst, cbytes));
-  CHECK(hipMemset(src, 0, rbytes));
+  hipLaunchKernelGGL(fill_kernel, dim3(cus * 8), dim3(256), 0, 0, (unsigned*)src, rbytes / 4);
+  CHECK(hipGetLastError());
+  CHECK(hipDeviceSynchronize());
   const int grid = cus * 8;
   CHECK(hipMalloc(&sink, (size_t)grid * 256 * sizeof(float)));
   const float ms_read = best_ms([&] {
