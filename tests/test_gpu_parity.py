@@ -31,8 +31,11 @@ TOL = {"f32": (1e-5, 1e-5), "bf16": (1e-2, 1e-3), "f16": (1e-2, 1e-3)}
 # normwise relative error of the outputs, ||gpu - oracle||_2 / ||oracle||_2 over
 # the checked rows: the absolute 1e-2 alone is a quarter of the outputs' RMS
 # at long contexts, so this second gate catches a wrong result that stays
-# small in absolute terms
-REL_GATE = {"f32": 1e-6, "bf16": 1e-2, "f16": 5e-3}
+# small in absolute terms. The fp32 gate is four times the largest error of a
+# plain fp32 evaluation of the step (every sum sequential, no fused multiply-add)
+# over the sweep's fp32 shapes, 1.3e-6 at 128 heads (tests/test_f32_gate.py):
+# a gate below that would fail correct fp32 arithmetic
+REL_GATE = {"f32": 5e-6, "bf16": 1e-2, "f16": 5e-3}
 
 
 def half_ulp(v, dtype):
