@@ -16,7 +16,7 @@ from tests.test_gpu_parity import check_partial, check_step, oracle_qlat, say
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 32
+N_CASES = 128
 
 
 def draw_case(i):
