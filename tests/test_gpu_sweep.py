@@ -3,7 +3,10 @@ partial call, each against the float64 oracle: batch sizes, head counts,
 query lengths, block sizes (paged 32 / 64 / 128 and contiguous), part
 counts, explicit and automatic split counts, ragged and empty ranges, and
 the three storage types; every other case with the split plan built on the
-host, and half the cases with a current chunk in the history call's launch. Sizes stay small enough for the oracle to finish in seconds per case."""
+host, and half the cases with a current chunk in the history call's launch.
+A second sweep covers query lengths up to 8 with a current chunk and
+sequences that share cache blocks. Sizes stay small enough for the oracle to
+finish in seconds per case."""
 import numpy as np
 import pytest
 import torch
@@ -63,3 +66,55 @@ def test_sweep_step_and_partial(i):
     L.mla_decode_partial(sp2.hist_args)
     torch.cuda.synchronize()
     check_partial(w, sp2, qs)
+
+
+# ---------------------------------------------------------------------------
+# multi-token decoding and shared cache blocks
+# ---------------------------------------------------------------------------
+
+def draw_mtp_case(i):
+    """Sweep case i of query lengths 1-8 (a current chunk for most S > 1),
+    bf16 / fp16, and whether the sequences share cache blocks, the current
+    chunk runs in the history's launch, and the plan is built on the host."""
+    r = np.random.Generator(np.random.PCG64(7000 + i))
+    dt = ["bf16", "f16"][i % 2]
+    S = int(r.integers(1, 9))
+    over = dict(B=int(r.integers(2, 6)), H=int(r.choice([16, 128, 130])), S=S, dtype=dt,
+                block_size=int(r.choice([16, 32, 64])), parts=int(r.integers(1, 5)),
+                lengths=("uniform", int(r.integers(50, 400)), int(r.integers(400, 2500))),
+                current=bool(S > 1 and r.random() < 0.8), part_out_dtype=dt,
+                part_lse_dtype=str(r.choice(["f32", dt])))
+    splits = int(r.choice([0, 0, 1, 2, 3]))
+    return over, splits, bool(r.random() < 0.6), bool(r.random() < 0.5), bool(r.random() < 0.5)
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_sweep_mtp_shared_blocks(i):
+    """Whole step and partial call against the oracle; with `share`, every
+    sequence after the first reads the first sequence's full cache blocks as
+    its prefix (one physical block in several block-table rows, as prefix
+    sharing makes it)."""
+    over, splits, share, pair, host = draw_mtp_case(i)
+    sp = W.spec(2 if over["dtype"] == "bf16" else 4, **over)
+    say(f"[sweep-mtp {i}] {over} splits={splits} share={share} pair={pair} host={host}")
+    w = W.make_workload(sp)
+    if share:
+        bs = sp.block_size
+        full0 = int(w.lengths[0]) // bs
+        for b in range(1, sp.B):
+            k = min(full0, int(w.lengths[b]) // bs)
+            w.block_table[b, :k] = w.block_table[0, :k]
+    st = DecodeStep(w, num_splits=splits, auto_plan=splits == 0, host_plan=host and splits == 0,
+                    pair_current=pair and sp.current)
+    st.run()
+    torch.cuda.synchronize()
+    extra = sp.part_lse_dtype if sp.part_lse_dtype != "f32" else None
+    heads = sorted(set(list(range(0, sp.H, max(1, sp.H // 5))) + [sp.H - 1]))
+    check_step(w, st, list(range(sp.B)), heads, extra)
+    qs = oracle_qlat(w)
+    st2 = DecodeStep(w, q_lat_in=qs, num_splits=splits, auto_plan=splits == 0)
+    st2.parts_out.fill_(float("nan"))
+    st2.parts_lse.fill_(float("nan"))
+    L.mla_decode_partial(st2.hist_args)
+    torch.cuda.synchronize()
+    check_partial(w, st2, qs)
