@@ -353,7 +353,9 @@ int mla_vup(const void* x, const void* w_uv, void* out, int T, int H, int dtype,
  *   w_uk [H][512][128], kv_new [T][576] (the new tokens' c_KV, then their
  *   k_R before rotation), all `dtype`.
  *   positions int32 [T] (DEVICE): the logical position of each new token in
- *   its sequence, used as the rotation angle and as its cache slot.
+ *   its sequence, used as the rotation angle and as its cache slot. The S
+ *   positions of one sequence must differ (two new tokens in one slot: which
+ *   token's row the slot ends up holding is unspecified).
  *   rope_theta > 0: rotary base.
  *   Cache: the same layout as mla_partial_args (paged: kv, block_table
  *   [B][max_blocks], block_size > 0, num_blocks; contiguous: block_table

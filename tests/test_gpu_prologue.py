@@ -56,7 +56,9 @@ def make_inputs(seed, dt, B, S, H, paged, bs=32, nblk=6, spare=3, stride=200):
         inp["block_table"] = None
         inp["cache"] = g(B * stride, D_C + D_R)
         cap = stride
-    pos = np.array([[int(r.integers(0, cap - S)) + s for s in range(S)] for b in range(B)],
+    # each sequence's new tokens at consecutive positions from a random start
+    # (distinct slots, as the prologue requires)
+    pos = np.array([int(r.integers(0, cap - S)) + np.arange(S) for b in range(B)],
                    np.int32).reshape(-1)
     pos[1] = cap + 7          # past the capacity: must not be written
     if T > 3:
@@ -186,3 +188,47 @@ def test_prologue_then_attention():
         excess = np.abs(go[sl][:, heads] - o) - half_ulp(o, dt)
         assert excess.max() <= 1e-2, (b, excess.max())
         assert np.abs(gl[sl][:, heads] - l).max() <= 1e-3, b
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_prologue_random_shapes(i):
+    """Seeded random shapes of the same check: fp32 / bf16 / fp16, paged
+    (block sizes 16-128, 1-39 blocks per sequence) or contiguous (strides to
+    5000), 1-6 sequences of 1-4 new tokens, 8-130 heads; positions up to a
+    few thousand (the rotation angle is reduced in double precision)."""
+    r = np.random.Generator(np.random.PCG64(3000 + i))
+    dt = ["bf16", "f16", "f32"][i % 3]
+    paged = bool(r.random() < 0.7)
+    B, S = int(r.integers(1, 7)), int(r.integers(1, 5))
+    if B * S < 2:  # the input builder marks token 1 invalid
+        S = 2
+    H = int(r.choice([8, 16, 64, 128, 130]))
+    bs = int(r.choice([16, 32, 64, 128]))
+    nblk = int(r.integers(1, 40))
+    stride = int(r.integers(S + 8, 5000))
+    if paged and nblk * bs < S + 8:
+        nblk = (S + 8) // bs + 1
+    inp = make_inputs(4000 + i, dt, B=B, S=S, H=H, paged=paged, bs=bs, nblk=nblk, stride=stride)
+    q_lat, q_rope, cache, before = run_gpu(inp, dt)
+    pos = inp["positions"]
+    ok = np.array([valid(inp, t) for t in range(B * S)])
+    ql, _, _ = mo.decode_prologue(inp["q_nope"], inp["q_pe"], inp["w_uk"], inp["kv_new"],
+                                  np.where(ok, pos, 0), inp["cache"], inp["block_table"],
+                                  inp["bs"], inp["stride"], B, S, D_C)
+    qr = mo.rope(inp["q_pe"], pos[:, None].astype(np.int64))
+    g_ql, g_qr = f64(q_lat), f64(q_rope)
+    assert np.all(np.abs(g_ql - ql) <= 2 * half_ulp(ql, dt) + (1e-4 if dt != "f32" else 1e-5))
+    assert np.all(np.abs(g_qr - qr) <= half_ulp(qr, dt) + ROT_TOL * (np.abs(qr) + 1))
+    got = f64(cache)
+    written = set()
+    for t in range(B * S):
+        if not ok[t]:
+            continue
+        row = mo.cache_slot(t // S, int(pos[t]), inp["block_table"], inp["bs"], inp["stride"])
+        written.add(row)
+        assert np.array_equal(got[row, :D_C], inp["kv_new"][t, :D_C])
+        want = mo.rope(inp["kv_new"][t, D_C:], int(pos[t]))
+        assert np.all(np.abs(got[row, D_C:] - want) <= half_ulp(want, dt) + ROT_TOL * (np.abs(want) + 1))
+    assert len(written) == int(ok.sum())  # distinct slots
+    others = np.array([rr for rr in range(got.shape[0]) if rr not in written])
+    assert torch.equal(cache[torch.from_numpy(others).cuda()], before[torch.from_numpy(others).cuda()])
