@@ -571,3 +571,73 @@ def test_side_stream_step(case):
         assert torch.equal(side.out, ser.out)
         assert torch.equal(side.final_lse(), ser.final_lse())
     check_step(w, side, seqs, heads, extra)
+
+
+def draw_combine_case(i):
+    r = np.random.Generator(np.random.PCG64(8000 + i))
+    dts = ["bf16", "f16", "f32"]
+    pdt, ldt = str(r.choice(dts)), str(r.choice(dts))
+    dt = ["bf16", "f16"][i % 2]
+    P = int(r.choice([1, 2, 3, 5, 8, 9, 12, 33, 64, 65, 80]))
+    local = bool(r.random() < 0.4)
+    H = int(r.choice([1, 3, 16, 64, 128]))
+    T = int(max(1, min(int(r.integers(1, 160)), 120000 // (P * H))))
+    return r, pdt, ldt, dt, P, local, T, H
+
+
+@pytest.mark.parametrize("i", range(32))
+def test_combine_vup_random(i):
+    """Seeded random merges: 1 to 80 parts (more than the 8 loaded ahead,
+    and more than the 64 LSEs one load round covers), a local part or not,
+    every storage type of parts and LSEs, 1 to 128 heads, ragged token
+    counts; scattered empty parts, fully empty rows and parts 80 above the
+    rest. mla_lse_combine against the oracle; mla_combine_vup bit for bit
+    equal to mla_lse_combine + mla_vup, and against the oracle's combine and
+    V-up within the storage rounding."""
+    r, pdt, ldt, dt, P, local, T, H = draw_combine_case(i)
+    say(f"[combine-random {i}] P={P} local={local} T={T} H={H} parts {pdt} lse {ldt} out {dt}")
+    outs = r.standard_normal((P, T, H, 512)) * 0.1
+    lses = r.uniform(-5, 15, size=(P, T, H))
+    empty = r.random((P, T, H)) < 0.05
+    lses[empty] = -np.inf
+    outs[empty] = 0
+    if T > 1:
+        lses[:, T - 1, 0] = -np.inf        # a fully empty row
+        outs[:, T - 1, 0] = 0
+    hot = r.random(P) < 0.15
+    lses[hot] += 80.0
+    o_s = W.round_to(outs, pdt)
+    l_s = np.where(np.isfinite(lses), W.round_to(np.where(np.isfinite(lses), lses, 0), ldt), -np.inf)
+    wuv = W.round_to(r.standard_normal((H, 512, 128)) / math.sqrt(512), dt)
+    n = P - 1 if local else P
+    dev = "cuda"
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16}[dt]
+    tp = to_device(W.to_storage(o_s, pdt), pdt, dev)
+    tl = to_device(W.to_storage(l_s, ldt), ldt, dev)
+    tw = to_device(W.to_storage(wuv, dt), dt, dev)
+    parts = (tp[:n].contiguous(), tl[:n].contiguous()) if n else (None, None)
+    loc = dict(local_out=tp[n].contiguous(), local_lse=tl[n].contiguous()) if local else {}
+    ref_o, ref_l = mo.lse_combine(o_s, l_s)
+    fin = np.isfinite(ref_l)
+    # the combine alone, fp32 output
+    c_out = torch.empty((T, H, 512), dtype=torch.float32, device=dev)
+    c_lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    L.mla_lse_combine(parts[0], parts[1], c_out, c_lse, **loc)
+    # two calls in the compute type, then the fused call
+    lat2 = torch.empty((T, H, 512), dtype=tdt, device=dev)
+    lse2 = torch.empty((T, H), dtype=torch.float32, device=dev)
+    out2 = torch.empty((T, H, 128), dtype=tdt, device=dev)
+    L.mla_lse_combine(parts[0], parts[1], lat2, lse2, **loc)
+    L.mla_vup(lat2, tw, out2)
+    lat = torch.full((T, H, 512), float("nan"), dtype=tdt, device=dev)
+    lse = torch.full((T, H), float("nan"), dtype=torch.float32, device=dev)
+    out = torch.full((T, H, 128), float("nan"), dtype=tdt, device=dev)
+    L.mla_combine_vup(parts[0], parts[1], tw, out, lse, lat_out=lat, **loc)
+    torch.cuda.synchronize()
+    go, gl = f64(c_out), f64(c_lse)
+    assert np.all(gl[~fin] == -np.inf) and np.all(go[~fin] == 0)
+    assert np.abs(go - ref_o).max() <= 1e-5
+    assert np.abs(gl[fin] - ref_l[fin]).max() <= 2e-5 * max(1.0, np.abs(ref_l[fin]).max())
+    assert torch.equal(out, out2) and torch.equal(lat, lat2) and torch.equal(lse, lse2)
+    ref = mo.v_up(W.round_to(ref_o, dt), wuv)
+    assert np.all(np.abs(f64(out) - ref) <= half_ulp(ref, dt) + 1e-3)
