@@ -497,10 +497,21 @@ def test_combine_vup_fused(pdt, ldt, dt, n, local, T, H):
     assert np.abs(f64(lse)[fin] - ref_l[fin]).max() <= 2e-5 * max(1.0, np.abs(ref_l[fin]).max())
 
 
-@pytest.mark.parametrize("dt", ["f32", "bf16", "f16"])
-def test_vup_and_absorb(dt):
-    r = np.random.Generator(np.random.PCG64(5))
-    T, H = 37, 24
+def _vup_absorb_shapes():
+    """(dt, T, H): the fixed case per type, then seeded random token and
+    head counts (token blocks of the matrix kernels cut anywhere, one head,
+    more than 128 heads)."""
+    cases = [(dt, 37, 24) for dt in ("f32", "bf16", "f16")]
+    r = np.random.Generator(np.random.PCG64(77))
+    for i in range(18):
+        cases.append((("f32", "bf16", "f16")[i % 3], int(r.choice([1, 2, 31, 33, 64, 127, 129, 300])),
+                      int(r.choice([1, 7, 16, 128, 130]))))
+    return cases
+
+
+@pytest.mark.parametrize("dt,T,H", _vup_absorb_shapes())
+def test_vup_and_absorb(dt, T, H):
+    r = np.random.Generator(np.random.PCG64(5 + T * 1000 + H))
     x = W.round_to(r.standard_normal((T, H, 512)) * 0.05, dt)
     wuv = W.round_to(r.standard_normal((H, 512, 128)) / math.sqrt(512), dt)
     qn = W.round_to(r.standard_normal((T, H, 128)), dt)
