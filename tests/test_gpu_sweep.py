@@ -75,7 +75,8 @@ def test_sweep_step_and_partial(i):
 def draw_mtp_case(i):
     """Sweep case i of query lengths 1-8 (a current chunk for most S > 1),
     bf16 / fp16, and whether the sequences share cache blocks, the current
-    chunk runs in the history's launch, and the plan is built on the host."""
+    chunk runs in the history's launch (else, in every other case, on a side
+    stream), and the plan is built on the host."""
     r = np.random.Generator(np.random.PCG64(7000 + i))
     dt = ["bf16", "f16"][i % 2]
     S = int(r.integers(1, 9))
@@ -104,8 +105,11 @@ def test_sweep_mtp_shared_blocks(i):
         for b in range(1, sp.B):
             k = min(full0, int(w.lengths[b]) // bs)
             w.block_table[b, :k] = w.block_table[0, :k]
+    # a current chunk not paired with the history runs on a side stream in
+    # every other such case
+    side = sp.current and not pair and i % 2 == 1
     st = DecodeStep(w, num_splits=splits, auto_plan=splits == 0, host_plan=host and splits == 0,
-                    pair_current=pair and sp.current)
+                    pair_current=pair and sp.current, side_stream=side)
     st.run()
     torch.cuda.synchronize()
     extra = sp.part_lse_dtype if sp.part_lse_dtype != "f32" else None
