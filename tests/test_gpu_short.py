@@ -84,7 +84,7 @@ def check_rows(dtype, ql, qr, kv, rs, re_, B, S, H, mask, go, gl, scale, out_dt,
             assert np.all(np.isfinite(g_o[fin])) and np.all(np.isfinite(g_l[fin]))
             err = (np.abs(g_o - o) - half_ulp(o, od))[fin]
             assert err.size == 0 or err.max() <= otol, (p, b, err.max())
-            assert np.all(np.abs(g_l - l)[fin] <= ltol + half_ulp(l[fin], lse_dt)), (p, b)
+            assert np.all(np.abs(g_l[fin] - l[fin]) <= ltol + half_ulp(l[fin], lse_dt)), (p, b)
 
 
 CASES = [
