@@ -254,7 +254,10 @@ size_t mla_decode_partial_workspace_size(const mla_partial_args* a);
  * more than 8 keys: the study page's CURRENT call over the q_len tokens of
  * the chunk), which runs on a vector kernel of one wave per (part, query)
  * and 4 heads with an exact fp32 softmax; fp32 (and MLA_FLAG_FORCE_SIMPLE)
- * runs on the plain kernel, one workgroup per (part, query, head). S <= 64
+ * runs on the plain kernel, one workgroup per (part, query, head), and so
+ * does a paged cache whose block_size is not a multiple of 32 (the matrix
+ * kernel's 32-key tiles must not straddle blocks); mla_decode_partial_plan
+ * reports the kernel a call takes (matrix_path). S <= 64
  * (MLA_ERR_UNSUPPORTED above).
  * Softmax range (K3 page, section 4.2: the online-softmax rescale is
  * mandatory): the matrix kernel exponentiates relative to a per-chunk
