@@ -298,3 +298,16 @@ def test_pair_valid_call_without_device_reports_hip_error():
     assert call_pair(hist, cur) == -7
     hist.flags = L.MLA_FLAG_FORCE_SIMPLE
     assert call_pair(hist, cur) == -6
+
+
+@pytest.mark.parametrize("block_size,path", [(32, 1), (64, 1), (128, 1), (16, 0), (48, 0), (8, 0)])
+def test_paged_block_size_routing(block_size, path):
+    """A paged bf16 call takes the matrix kernel when its block size is a
+    multiple of the kernel's 32-key tile, else the plain kernel (no
+    workspace, no host plan); the plan query reports which."""
+    a = base_args(block_size=block_size, max_blocks=256 // block_size + 1)
+    n = a.P * a.B
+    info = L.mla_decode_partial_plan(a, [0] * n, [200] * n)
+    assert info.matrix_path == path
+    assert (L.mla_decode_partial_workspace_size(a) == 0) == (path == 0)
+    assert (L.mla_decode_partial_plan_words(a) == 0) == (path == 0)
