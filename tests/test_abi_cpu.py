@@ -300,7 +300,8 @@ def test_pair_valid_call_without_device_reports_hip_error():
     assert call_pair(hist, cur) == -6
 
 
-@pytest.mark.parametrize("block_size,path", [(32, 1), (64, 1), (128, 1), (16, 0), (48, 0), (8, 0)])
+@pytest.mark.parametrize("block_size,path", [(32, 1), (64, 1), (128, 1), (16, 0), (48, 0),
+                                             (8, 0), (24, 0), (40, 0)])
 def test_paged_block_size_routing(block_size, path):
     """A paged bf16 call takes the matrix kernel when its block size is a
     multiple of the kernel's 32-key tile, else the plain kernel (no

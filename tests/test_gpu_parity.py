@@ -325,6 +325,37 @@ def test_partial_edge_ranges(flags, splits):
     check_partial(w, st, qs, ranges=(rs, re))
 
 
+@pytest.mark.parametrize("bs", [16, 48, 32, 64, 0])
+@pytest.mark.parametrize("dtype,splits", [("bf16", 0), ("f16", 3), ("bf16", 1)])
+def test_partial_block_sizes_unaligned_starts(bs, dtype, splits):
+    """Paged caches of 32- and 64-row blocks and a contiguous cache on the
+    matrix kernel, 16- and 48-row blocks on the plain kernel (a 32-key tile
+    would span two blocks), with seeded random ranges whose starts fall
+    anywhere inside a block, some ending inside the first tile. Outputs
+    poisoned with NaN first; every row against the oracle."""
+    wid = 2 if dtype == "bf16" else 4
+    sp = W.spec(wid, B=5, lengths=("uniform", 300, 900), parts=3, block_size=bs,
+                part_out_dtype=dtype, part_lse_dtype="f32")
+    say(f"[block-size {bs}] {dtype} splits={splits}")
+    w = W.make_workload(sp)
+    r = np.random.Generator(np.random.PCG64(600 + bs))
+    rs = np.zeros((sp.parts, sp.B), np.int32)
+    re = np.zeros((sp.parts, sp.B), np.int32)
+    for b in range(sp.B):
+        n = int(w.lengths[b])
+        cuts = np.sort(r.integers(0, n + 1, size=2 * sp.parts))
+        rs[:, b], re[:, b] = cuts[0::2], cuts[1::2]
+    rs[0, 0], re[0, 0] = 17, 29      # inside one tile, after its 16-row boundary
+    rs[1, 1], re[1, 1] = 50, 51      # a single key
+    qs = oracle_qlat(w)
+    info = L.mla_decode_partial_plan(
+        DecodeStep(w, q_lat_in=qs).hist_args, rs.reshape(-1), re.reshape(-1))
+    assert info.matrix_path == (1 if bs % 32 == 0 else 0)
+    st = run_partial(w, qs, num_splits=splits, ranges=(rs, re))
+    assert torch.isfinite(st.parts_out).all().item()
+    check_partial(w, st, qs, ranges=(rs, re))
+
+
 @pytest.mark.parametrize("flags,splits", EDGE_PATHS)
 def test_partial_invalid_metadata_is_contained(flags, splits):
     """A range past the table or a bad block id poisons only its own
